@@ -1,0 +1,131 @@
+"""CPU oracle for exact attention forward — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
+this package. The GPU library never imports, links or calls it, and this package imports nothing
+from the GPU package: the two share only the seeded input generator, which holds none of the
+method's arithmetic.
+
+The arithmetic lives in ``fa_ref.c`` (plain C, double precision, OpenMP over rows). It is the
+naive, two-pass definition of attention on the bf16 inputs:
+
+* scores ``S = scale * Q K^T``, a row softmax, then ``P V`` (learn-llm.fim.ai
+  "手写 FlashAttention：拆开 SDPA 这个黑盒", STEP 1);
+* the row maximum is subtracted before ``exp`` (same page, STEP 2);
+* with a causal mask only keys ``j <= i`` are visible to query ``i`` (same page, STEP 3);
+* the natural-log logsumexp of each row's visible scaled scores is returned alongside ``O``
+  (same page, STEP 4, the note on what the forward saves for the backward).
+
+Every function here is pinned by the ``not gpu`` tests in ``tests/test_oracle_pins.py``
+against closed forms, invariants and library special cases.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fa_ref.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``fa_ref.c`` into ``liboracle.so`` next to it (gcc, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
+               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=False)
+    lib = ctypes.CDLL(_LIB_PATH)
+    p_u16 = ctypes.POINTER(ctypes.c_uint16)
+    p_f64 = ctypes.POINTER(ctypes.c_double)
+    p_i64 = ctypes.POINTER(ctypes.c_int64)
+    i64 = ctypes.c_int64
+    lib.fa_ref_fwd.argtypes = [p_u16, p_u16, p_u16, p_f64, p_f64, i64, i64, i64, i64,
+                               ctypes.c_int, ctypes.c_double, ctypes.c_int]
+    lib.fa_ref_fwd.restype = ctypes.c_int
+    lib.fa_ref_fwd_rows.argtypes = [p_u16, p_u16, p_u16, i64, i64, i64, i64, ctypes.c_int,
+                                    ctypes.c_double, p_i64, i64, p_f64, p_f64, ctypes.c_int]
+    lib.fa_ref_fwd_rows.restype = ctypes.c_int
+    lib.fa_ref_threads_used.argtypes = [ctypes.c_int]
+    lib.fa_ref_threads_used.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _as_bf16_bits(x: np.ndarray, name: str) -> np.ndarray:
+    if x.dtype != np.uint16:
+        raise TypeError(f"{name}: expected bf16 bit patterns as uint16, got {x.dtype}")
+    if x.ndim != 4:
+        raise ValueError(f"{name}: expected [B, H, T, d], got shape {x.shape}")
+    return np.ascontiguousarray(x)
+
+
+def _ptr(a: np.ndarray, ctype):
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def threads_used(num_threads: int = 0) -> int:
+    """Threads an OpenMP team of the oracle actually gets for ``num_threads`` (0: default)."""
+    return int(_load().fa_ref_threads_used(int(num_threads)))
+
+
+def attention_fwd(q_bits, k_bits, v_bits, causal: bool, scale: float, num_threads: int = 0):
+    """Exact attention forward on bf16 inputs given as uint16 bit patterns ``[B, H, T, d]``.
+
+    Returns ``(o, lse)``: ``o`` float64 ``[B, H, T, d]`` and ``lse`` float64 ``[B, H, T]``
+    (natural log of the row's sum of ``exp`` over the visible scaled scores).
+    """
+    q = _as_bf16_bits(q_bits, "q")
+    k = _as_bf16_bits(k_bits, "k")
+    v = _as_bf16_bits(v_bits, "v")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q/k/v shapes differ: {q.shape} {k.shape} {v.shape}")
+    B, H, T, d = q.shape
+    o = np.empty((B, H, T, d), dtype=np.float64)
+    lse = np.empty((B, H, T), dtype=np.float64)
+    rc = _load().fa_ref_fwd(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                            _ptr(v, ctypes.c_uint16), _ptr(o, ctypes.c_double),
+                            _ptr(lse, ctypes.c_double), B, H, T, d, int(bool(causal)),
+                            float(scale), int(num_threads))
+    if rc != 0:
+        raise RuntimeError(f"fa_ref_fwd failed with code {rc}")
+    return o, lse
+
+
+def attention_rows(q_bits, k_bits, v_bits, causal: bool, scale: float, rows, num_threads: int = 0):
+    """Exact attention forward for selected rows only.
+
+    ``rows`` holds flat row indices ``(b*H + h)*T + i``. Returns ``(o, lse)`` with ``o`` float64
+    ``[len(rows), d]`` and ``lse`` float64 ``[len(rows)]``.
+    """
+    q = _as_bf16_bits(q_bits, "q")
+    k = _as_bf16_bits(k_bits, "k")
+    v = _as_bf16_bits(v_bits, "v")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q/k/v shapes differ: {q.shape} {k.shape} {v.shape}")
+    B, H, T, d = q.shape
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1))
+    o = np.empty((r.size, d), dtype=np.float64)
+    lse = np.empty((r.size,), dtype=np.float64)
+    rc = _load().fa_ref_fwd_rows(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                                 _ptr(v, ctypes.c_uint16), B, H, T, d, int(bool(causal)),
+                                 float(scale), _ptr(r, ctypes.c_int64), r.size,
+                                 _ptr(o, ctypes.c_double), _ptr(lse, ctypes.c_double),
+                                 int(num_threads))
+    if rc != 0:
+        raise RuntimeError(f"fa_ref_fwd_rows failed with code {rc}")
+    return o, lse
