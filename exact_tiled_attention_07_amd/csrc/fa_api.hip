@@ -1,0 +1,162 @@
+// Host side of libfa.so: argument checks, the tile table, the launch plan and the kernel launch.
+// Declarations and the contract of every entry point are in include/fa.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "fa.h"
+#include "fa_kernel.hpp"
+
+namespace {
+
+using KernelFn = void (*)(const __bf16*, const __bf16*, const __bf16*, __bf16*, float*, int, int, int,
+                          float);
+
+struct TileEntry {
+  int d, block_m, block_n, waves;
+  KernelFn causal_fn, full_fn;
+  int lds_bytes;
+};
+
+template <int D, int QB, int NW, int BN>
+constexpr TileEntry entry() {
+  using Cc = fa::Cfg<D, QB, NW, BN, true>;
+  using Cf = fa::Cfg<D, QB, NW, BN, false>;
+  return TileEntry{D, Cc::BM, BN, NW, &fa::fa_fwd_kernel<Cc>, &fa::fa_fwd_kernel<Cf>, Cc::LDS_BYTES};
+}
+
+// Supported tile shapes. The first entry for each d is the default (see default_tile()).
+const TileEntry kTiles[] = {
+    entry<64, 1, 4, 64>(),   // d=64: 128 queries (4 waves x 32), 64-key tiles
+    entry<64, 1, 2, 64>(),   // d=64: 64 x 64, the tile shape of the tutorial page
+    entry<64, 2, 2, 64>(),   // d=64: 128 queries (2 waves x 64)
+    entry<64, 2, 4, 64>(),   // d=64: 256 queries (4 waves x 64)
+    entry<64, 1, 8, 64>(),   // d=64: 256 queries (8 waves x 32)
+    entry<128, 1, 4, 64>(),  // d=128: 128 queries (4 waves x 32), 64-key tiles
+    entry<128, 1, 2, 64>(),  // d=128: 64 x 64
+};
+
+const TileEntry* find_tile(int d, int block_m, int block_n, int waves) {
+  for (const TileEntry& t : kTiles)
+    if (t.d == d && t.block_m == block_m && t.block_n == block_n && t.waves == waves) return &t;
+  return nullptr;
+}
+
+const TileEntry* default_tile(int d, int /*T*/, int /*causal*/) {
+  for (const TileEntry& t : kTiles)
+    if (t.d == d) return &t;
+  return nullptr;
+}
+
+int check_sizes(int B, int H, int T, int d) {
+  if (B < 0 || H < 0 || T < 0) return FA_ERR_INVALID_ARG;
+  if (T > FA_MAX_T) return FA_ERR_INVALID_ARG;
+  if ((int64_t)B * H > FA_MAX_BH) return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED_D;
+  return FA_OK;
+}
+
+int resolve_tile(int d, int T, int causal, int block_m, int block_n, int waves, const TileEntry** out) {
+  if (block_m == 0 && block_n == 0 && waves == 0) {
+    *out = default_tile(d, T, causal);
+  } else {
+    if (block_m <= 0 || block_n <= 0 || waves <= 0) return FA_ERR_TILE;
+    *out = find_tile(d, block_m, block_n, waves);
+  }
+  return *out ? FA_OK : FA_ERR_TILE;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+  return na && nb && x < y + nb && y < x + na;
+}
+
+int launch(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int T, int d,
+           int causal, float scale, void* stream, int block_m, int block_n, int waves) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int rc = check_sizes(B, H, T, d);
+  if (rc != FA_OK) return rc;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  const TileEntry* tile = nullptr;
+  rc = resolve_tile(d, T, causal, block_m, block_n, waves, &tile);
+  if (rc != FA_OK) return rc;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGNMENT;
+  if ((uintptr_t)lse & 3u) return FA_ERR_ALIGNMENT;
+  const size_t n_elem = (size_t)B * H * T * d;
+  const size_t bytes = n_elem * 2, lse_bytes = (size_t)B * H * T * 4;
+  if (overlaps(o, bytes, q, bytes) || overlaps(o, bytes, k, bytes) || overlaps(o, bytes, v, bytes) ||
+      overlaps(lse, lse_bytes, q, bytes) || overlaps(lse, lse_bytes, k, bytes) ||
+      overlaps(lse, lse_bytes, v, bytes) || overlaps(lse, lse_bytes, o, bytes))
+    return FA_ERR_INVALID_ARG;
+  if (n_elem == 0) return FA_OK;
+
+  const int nq = (T + tile->block_m - 1) / tile->block_m;
+  const int BH = B * H;
+  const int64_t grid = (int64_t)nq * BH;
+  if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  const float scale_log2 = scale * fa::kLog2e;
+  KernelFn fn = causal ? tile->causal_fn : tile->full_fn;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * tile->waves), 0, (hipStream_t)stream,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, T, nq, BH,
+                     scale_log2);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int T, int d,
+           int causal, float scale, void* stream) {
+  return launch(q, k, v, o, lse, B, H, T, d, causal, scale, stream, 0, 0, 0);
+}
+
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int T,
+              int d, int causal, float scale, void* stream, int block_m, int block_n, int waves) {
+  if (block_m == 0 && block_n == 0 && waves == 0) return FA_ERR_TILE;
+  return launch(q, k, v, o, lse, B, H, T, d, causal, scale, stream, block_m, block_n, waves);
+}
+
+int fa_fwd_plan(int B, int H, int T, int d, int causal, int block_m, int block_n, int waves,
+                fa_plan_info* out) {
+  if (!out) return FA_ERR_NULL;
+  int rc = check_sizes(B, H, T, d);
+  if (rc != FA_OK) return rc;
+  const TileEntry* tile = nullptr;
+  rc = resolve_tile(d, T, causal, block_m, block_n, waves, &tile);
+  if (rc != FA_OK) return rc;
+  fa_plan_info p;
+  p.block_m = tile->block_m;
+  p.block_n = tile->block_n;
+  p.waves = tile->waves;
+  p.q_blocks = (T + tile->block_m - 1) / tile->block_m;
+  p.grid = (long long)p.q_blocks * B * H;
+  p.lds_bytes = tile->lds_bytes;
+  // K/V tiles per Q block: up to the diagonal when causal, all of them otherwise.
+  long long tiles_per_head = 0;
+  for (int qb = 0; qb < p.q_blocks; ++qb) {
+    const int kv_end = causal ? std::min((qb + 1) * tile->block_m, T) : T;
+    tiles_per_head += (kv_end + tile->block_n - 1) / tile->block_n;
+  }
+  p.kv_tiles = tiles_per_head * B * H;
+  *out = p;
+  return FA_OK;
+}
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_INVALID_ARG: return "invalid argument (size out of range, scale not finite and > 0, or overlapping buffers)";
+    case FA_ERR_UNSUPPORTED_D: return "unsupported head dimension (d must be 64 or 128)";
+    case FA_ERR_ALIGNMENT: return "misaligned pointer (q, k, v, o need 16 bytes; lse needs 4)";
+    case FA_ERR_HIP: return "HIP runtime error at kernel launch";
+    case FA_ERR_TILE: return "tile shape not in the supported table";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

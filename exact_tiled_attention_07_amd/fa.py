@@ -1,0 +1,163 @@
+"""ctypes binding of libfa.so (include/fa.h): argument marshalling only.
+
+Every step of the attention forward runs in the gfx950 HIP kernel behind ``fa_fwd``; this module
+checks tensor metadata, allocates outputs with torch when the caller gives none, and passes raw
+device pointers plus the current HIP stream. There is no fallback: if ``libfa.so`` is missing or
+a call fails, it raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "fa.h")
+
+FA_OK = 0
+FA_ERR_NULL = -1
+FA_ERR_INVALID_ARG = -2
+FA_ERR_UNSUPPORTED_D = -3
+FA_ERR_ALIGNMENT = -4
+FA_ERR_HIP = -5
+FA_ERR_TILE = -6
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"fa status {status}: {message}")
+        self.status = status
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("waves", ctypes.c_int),
+                ("q_blocks", ctypes.c_int), ("grid", ctypes.c_longlong),
+                ("lds_bytes", ctypes.c_int), ("kv_tiles", ctypes.c_longlong)]
+
+
+def lib():
+    """Load libfa.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FileNotFoundError(
+            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    L.fa_fwd.restype = i
+    L.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, i, i]
+    L.fa_fwd_ex.restype = i
+    L.fa_fwd_plan.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(PlanInfo)]
+    L.fa_fwd_plan.restype = i
+    L.fa_strerror.argtypes = [i]
+    L.fa_strerror.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def header_functions():
+    """Names of the functions include/fa.h declares."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(fa_\w+)\s*\(", text, flags=re.M)))
+
+
+def strerror(status: int) -> str:
+    return lib().fa_strerror(int(status)).decode()
+
+
+def _check(status: int):
+    if status != FA_OK:
+        raise FaError(status, strerror(status))
+
+
+def plan(B: int, H: int, T: int, d: int, causal: bool = True, block_m: int = 0, block_n: int = 0,
+         waves: int = 0) -> dict:
+    """Launch plan (tile shape, grid, LDS bytes, K/V tiles) that fa_fwd / fa_fwd_ex would use."""
+    info = PlanInfo()
+    _check(lib().fa_fwd_plan(B, H, T, d, int(bool(causal)), block_m, block_n, waves, ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in PlanInfo._fields_}
+
+
+def _check_inputs(q, k, v):
+    import torch
+
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor")
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16, got {t.dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be [B, H, T, d], got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    if not (q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on the same device")
+
+
+def _outputs(q, out, lse):
+    import torch
+
+    B, H, T, d = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.dtype != torch.bfloat16 or out.shape != q.shape or not out.is_contiguous()
+          or out.device != q.device):
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    elif (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous()
+          or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, T] on q's device")
+    return out, lse
+
+
+def _stream_handle(device, stream):
+    import torch
+
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def fwd(q, k, v, causal: bool = True, scale: float | None = None, out=None, lse=None, stream=None):
+    """Exact attention forward on the GPU: returns ``(o, lse)``.
+
+    q, k, v: contiguous bfloat16 ``[B, H, T, d]`` GPU tensors (d = 64 or 128). ``o`` is bfloat16
+    like q; ``lse`` is float32 ``[B, H, T]`` (natural log). ``scale`` defaults to 1/sqrt(d).
+    Launches on ``stream`` (a torch stream; default: the current stream of q's device).
+    """
+    import torch
+
+    _check_inputs(q, k, v)
+    out, lse = _outputs(q, out, lse)
+    B, H, T, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        _check(lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                            B, H, T, d, int(bool(causal)), scale, _stream_handle(q.device, stream)))
+    return out, lse
+
+
+def fwd_ex(q, k, v, block_m: int, block_n: int, waves: int, causal: bool = True,
+           scale: float | None = None, out=None, lse=None, stream=None):
+    """``fwd`` with the tile shape forced (``fa_fwd_ex``), for the tile-shape study."""
+    import torch
+
+    _check_inputs(q, k, v)
+    out, lse = _outputs(q, out, lse)
+    B, H, T, d = q.shape
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        _check(lib().fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), B, H, T, d, int(bool(causal)), scale,
+                               _stream_handle(q.device, stream), block_m, block_n, waves))
+    return out, lse

@@ -1,0 +1,110 @@
+/*
+ * fa.h — C-ABI of the MI355X (gfx950) exact tiled attention forward library (libfa.so).
+ *
+ * The one operation is the fused, tiled, exact attention forward
+ *
+ *     O[b,h,i,:] = sum_j P[i,j] V[b,h,j,:],   P[i,:] = softmax_j( scale * Q[b,h,i,:] . K[b,h,j,:] )
+ *     LSE[b,h,i] = ln sum_j exp( scale * Q[b,h,i,:] . K[b,h,j,:] )
+ *
+ * over the visible keys j (all j < T, or j <= i with the causal mask), computed block by block with
+ * the online softmax so that the T x T score matrix never reaches HBM:
+ *   - the naive definition and why the T x T matrix is the problem: learn-llm.fim.ai
+ *     "手写 FlashAttention：拆开 SDPA 这个黑盒", STEP 1;
+ *   - the online max / sum recurrence and the deferred division by l: same page, STEP 2;
+ *   - one program per Q block walking the K/V blocks, causal blocks above the diagonal skipped:
+ *     same page, STEP 3;
+ *   - exp2 with log2(e) folded into the scale, and the per-row logsumexp kept for a backward pass:
+ *     same page, STEP 4;
+ *   - the Q-block-parallel ordering that keeps m and l on chip: cnblogs
+ *     "内核案例研究：Flash Attention", section "块稀疏注意力 V2 和 V3".
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are row-major and contiguous. q, k, v and o are bf16 [B, H, T, d] (the innermost
+ *     dimension is d); lse is fp32 [B, H, T]. All of them are device pointers.
+ *   - The caller owns every buffer. The library never allocates, frees or keeps a pointer after the
+ *     call returns. o and lse must not overlap q, k, v or each other.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default stream). They return
+ *     after enqueueing the kernel and never synchronise. The library keeps no mutable global state
+ *     and is safe to call from several host threads.
+ *   - Arguments are checked before anything is launched; on any error nothing is written.
+ *   - B*H*T == 0 is a valid empty problem: FA_OK, nothing launched, nothing written.
+ *   - Inputs must be finite. NaN or Inf inputs give unspecified outputs (no error is raised).
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa_status {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,           /* a required pointer is NULL */
+  FA_ERR_INVALID_ARG = -2,    /* negative size, size too large, scale not finite and > 0, overlap */
+  FA_ERR_UNSUPPORTED_D = -3,  /* head dim d is not 64 or 128 */
+  FA_ERR_ALIGNMENT = -4,      /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
+  FA_ERR_HIP = -5,            /* the HIP runtime reported an error at launch */
+  FA_ERR_TILE = -6            /* fa_fwd_ex / fa_fwd_plan: tile shape not in the supported table */
+} fa_status;
+
+/* Largest accepted sequence length and largest accepted B*H (checked by every entry point). */
+#define FA_MAX_T (1 << 22)
+#define FA_MAX_BH (1 << 24)
+
+/*
+ * fa_fwd — exact attention forward.
+ *   q, k, v  [in]  bf16 [B, H, T, d], device, 16-byte aligned
+ *   o        [out] bf16 [B, H, T, d], device, 16-byte aligned; rounded to nearest even
+ *   lse      [out] fp32 [B, H, T], device, 4-byte aligned; natural-log logsumexp of each row's
+ *                  scaled scores over its visible keys
+ *   B, H, T  batch, heads, sequence length (queries and keys both have length T); >= 0,
+ *            T <= FA_MAX_T, B*H <= FA_MAX_BH
+ *   d        head dimension: 64 or 128
+ *   causal   nonzero: query i sees keys 0..i (the causal mask); zero: it sees all T keys
+ *   scale    finite and > 0; the scores are scale * q.k (1/sqrt(d) for standard attention)
+ *   stream   hipStream_t to launch on (NULL: default stream)
+ * Returns FA_OK or a negative fa_status.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int T,
+           int d, int causal, float scale, void* stream);
+
+/*
+ * fa_fwd_ex — fa_fwd with the tile shape forced, for the tile-shape study.
+ *   block_m  query rows per workgroup (a multiple of 32 * waves)
+ *   block_n  keys per K/V tile staged in LDS
+ *   waves    64-lane wavefronts per workgroup
+ * The supported (d, block_m, block_n, waves) combinations are those fa_fwd_plan accepts; any other
+ * returns FA_ERR_TILE. Otherwise identical to fa_fwd (same arguments, errors and results).
+ */
+int fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int T,
+              int d, int causal, float scale, void* stream, int block_m, int block_n, int waves);
+
+/* Launch plan of one call: what fa_fwd (or fa_fwd_ex) would launch. Host-only; no HIP call. */
+typedef struct fa_plan_info {
+  int block_m;     /* query rows per workgroup */
+  int block_n;     /* keys per K/V tile */
+  int waves;       /* wavefronts per workgroup */
+  int q_blocks;    /* ceil(T / block_m) */
+  long long grid;  /* workgroups launched: q_blocks * B * H (one per (Q block, batch*head)) */
+  int lds_bytes;   /* LDS per workgroup: double-buffered K and V tiles */
+  long long kv_tiles; /* K/V tiles processed by all workgroups (fully masked ones skipped) */
+} fa_plan_info;
+
+/*
+ * fa_fwd_plan — fill *out with the launch plan for these sizes.
+ *   block_m, block_n, waves: all 0 for the default table entry, or all > 0 to ask about a forced
+ *   shape (as fa_fwd_ex would use it).
+ * Returns FA_OK, FA_ERR_NULL (out NULL), FA_ERR_INVALID_ARG (bad sizes), FA_ERR_UNSUPPORTED_D or
+ * FA_ERR_TILE. Sizes may be zero (then grid and kv_tiles are 0).
+ */
+int fa_fwd_plan(int B, int H, int T, int d, int causal, int block_m, int block_n, int waves,
+                fa_plan_info* out);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,130 @@
+"""C-ABI of libfa.so on the host: symbols, argument checks, plans. No kernel is ever launched here.
+
+Every call below either fails validation or is an empty problem, and both return before any HIP
+call, so these run without a GPU.
+"""
+import ctypes
+import json
+import os
+
+import pytest
+
+from exact_tiled_attention_07_amd import fa
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")
+A = 0x10000  # fake, 16-byte-aligned, non-overlapping "device" addresses; never dereferenced
+
+
+def call(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=1, T=8, d=64, causal=1, scale=0.125):
+    return fa.lib().fa_fwd(q, k, v, o, lse, B, H, T, d, causal, scale, None)
+
+
+def test_library_exports_every_declared_function():
+    names = fa.header_functions()
+    assert names == ["fa_fwd", "fa_fwd_ex", "fa_fwd_plan", "fa_strerror"]
+    lib = fa.lib()
+    for n in names:
+        assert hasattr(lib, n)
+
+
+def test_null_pointers():
+    for kw in ("q", "k", "v", "o", "lse"):
+        assert call(**{kw: None}) == fa.FA_ERR_NULL
+
+
+@pytest.mark.parametrize("kw,val", [("B", -1), ("H", -1), ("T", -1), ("T", (1 << 22) + 1)])
+def test_bad_sizes(kw, val):
+    assert call(**{kw: val}) == fa.FA_ERR_INVALID_ARG
+
+
+def test_too_many_heads():
+    assert call(B=1 << 13, H=1 << 12) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("d", [0, 16, 32, 63, 65, 96, 256])
+def test_unsupported_head_dim(d):
+    assert call(d=d) == fa.FA_ERR_UNSUPPORTED_D
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("inf"), float("nan")])
+def test_bad_scale(scale):
+    assert call(scale=scale) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw,val", [("q", A + 8), ("k", 2 * A + 2), ("v", 3 * A + 4), ("o", 4 * A + 1),
+                                    ("lse", 5 * A + 2)])
+def test_misaligned(kw, val):
+    assert call(**{kw: val}) == fa.FA_ERR_ALIGNMENT
+
+
+def test_lse_only_needs_4_bytes():
+    # passes every check and is empty (T=0), so nothing is launched
+    assert call(lse=5 * A + 4, T=0) == fa.FA_OK
+
+
+@pytest.mark.parametrize("o,lse", [(A, 5 * A), (A + 512, 5 * A), (4 * A, 3 * A + 16), (4 * A, 4 * A + 64)])
+def test_overlapping_outputs(o, lse):
+    # q/k/v occupy [A, A+1024), ... with T=8, d=64 (1 KiB each)
+    assert call(o=o, lse=lse) == fa.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("shape", [(0, 3, 8, 64), (2, 0, 8, 64), (2, 3, 0, 128)])
+def test_empty_problem_is_ok(shape):
+    B, H, T, d = shape
+    assert call(B=B, H=H, T=T, d=d) == fa.FA_OK
+    assert call(B=B, H=H, T=T, d=d, causal=0) == fa.FA_OK
+
+
+def test_fwd_ex_tile_checks():
+    L = fa.lib()
+    args = (A, 2 * A, 3 * A, 4 * A, 5 * A, 1, 1, 0, 64, 1, 0.125, None)
+    assert L.fa_fwd_ex(*args, 0, 0, 0) == fa.FA_ERR_TILE        # must force a shape
+    assert L.fa_fwd_ex(*args, 96, 64, 3) == fa.FA_ERR_TILE       # not in the table
+    assert L.fa_fwd_ex(*args, 64, 64, -2) == fa.FA_ERR_TILE
+    assert L.fa_fwd_ex(*args, 64, 64, 2) == fa.FA_OK             # supported, empty problem
+    args128 = (A, 2 * A, 3 * A, 4 * A, 5 * A, 1, 1, 0, 128, 1, 0.125, None)
+    assert L.fa_fwd_ex(*args128, 128, 64, 4) == fa.FA_OK
+
+
+def test_strerror_covers_codes():
+    seen = set()
+    for code in range(-6, 1):
+        s = fa.strerror(code)
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 7
+    assert fa.strerror(-99) == "unknown status"
+
+
+def test_plan_matches_the_pages_launch_count():
+    fact = json.load(open(GOLDEN))["programs_T4096"]
+    p = fa.plan(fact["B"], fact["H"], fact["T"], 64, True, fact["block_m"], fact["block_n"], 2)
+    assert p["grid"] == fact["programs"] == 3072
+    assert p["q_blocks"] == 64
+
+
+def test_plan_default_and_tile_counts():
+    p = fa.plan(4, 12, 4096, 64, True)
+    assert p["block_m"] % (32 * p["waves"]) == 0
+    nq = -(-4096 // p["block_m"])
+    assert p["q_blocks"] == nq and p["grid"] == nq * 48
+    # causal: Q block i needs ceil(min((i+1)*BM, T) / BN) tiles
+    bm, bn = p["block_m"], p["block_n"]
+    expect = sum(-(-min((i + 1) * bm, 4096) // bn) for i in range(nq)) * 48
+    assert p["kv_tiles"] == expect
+    full = fa.plan(4, 16, 8192, 128, False)
+    assert full["kv_tiles"] == full["grid"] * (-(-8192 // full["block_n"]))
+    assert full["lds_bytes"] == 4 * full["block_n"] * 128 * 2
+    ragged = fa.plan(2, 12, 1000, 64, True)
+    assert ragged["q_blocks"] == -(-1000 // ragged["block_m"])
+    assert fa.plan(0, 12, 1000, 64, True)["grid"] == 0
+
+
+def test_plan_errors():
+    with pytest.raises(fa.FaError) as e:
+        fa.plan(1, 1, 8, 80)
+    assert e.value.status == fa.FA_ERR_UNSUPPORTED_D
+    with pytest.raises(fa.FaError) as e:
+        fa.plan(1, 1, 8, 64, True, 96, 64, 3)
+    assert e.value.status == fa.FA_ERR_TILE
+    assert fa.lib().fa_fwd_plan(1, 1, 8, 64, 1, 0, 0, 0, None) == fa.FA_ERR_NULL

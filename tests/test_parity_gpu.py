@@ -1,0 +1,212 @@
+"""Parity of the gfx950 HIP kernel (through the C-ABI) with the CPU fp64 oracle, element by element.
+
+Small and medium problems are compared in full; the large ones (T = 4096, 16384 and the d = 128
+non-causal case) are computed in full on the GPU with the default launch configuration and checked
+on sampled rows that the oracle evaluates one by one. Every input is seeded.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exact_tiled_attention_07_amd as fa
+from exact_tiled_attention_07_amd.inputs import WORKLOADS, bf16_bits_from_f32, bf16_bits_to_f32, make_qkv, to_torch_bf16
+
+from parity import assert_parity, compare
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_gpu(qb, kb, vb, causal, scale, **kw):
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale, **kw)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def run_gpu_ex(qb, kb, vb, causal, scale, bm, bn, w):
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    o, lse = fa.fwd_ex(q, k, v, bm, bn, w, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def full_check(qb, kb, vb, causal, scale, label):
+    say(f"[gpu] {label} shape={qb.shape} causal={causal} scale={scale}")
+    o, lse = run_gpu(qb, kb, vb, causal, scale)
+    o_ref, lse_ref = oracle.attention_fwd(qb, kb, vb, causal, scale)
+    stats = compare(o, lse, o_ref, lse_ref)
+    say(f"[gpu] {label} {stats}")
+    assert_parity(stats, label)
+    return o, lse, stats
+
+
+def sample_rows(B, H, T, n_random, seed):
+    """First and last rows of every head, a band around T/2, and random rows."""
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for bh in range(B * H):
+        base = bh * T
+        for i in (0, 1, 2, 63, 64, 127, 128, T // 2, T - 2, T - 1):
+            if 0 <= i < T:
+                rows.add(base + i)
+    rows.update(rng.integers(0, B * H * T, size=n_random).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_configs_full(name):
+    wl = WORKLOADS[name]
+    qb, kb, vb = wl.make()
+    o, _, stats = full_check(qb, kb, vb, wl.causal, wl.scale, wl.name)
+    # causal row 0 sees only key 0: exp2(0) = 1, masked p = 0, so O[0] is V[0] bit for bit
+    np.testing.assert_array_equal(o[:, :, 0, :], bf16_bits_to_f32(vb)[:, :, 0, :])
+    assert stats["n_ulp_clause"] == 0
+
+
+@pytest.mark.parametrize("name", ["c4", "c5a", "c5b"])
+def test_configs_sampled(name):
+    wl = WORKLOADS[name]
+    say(f"[gpu] {wl.name}: generating inputs")
+    qb, kb, vb = wl.make()
+    say(f"[gpu] {wl.name}: GPU forward (full problem, default launch)")
+    o, lse = run_gpu(qb, kb, vb, wl.causal, wl.scale)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    rows = sample_rows(wl.B, wl.H, wl.T, 1500, seed=wl.seed)
+    say(f"[gpu] {wl.name}: oracle on {rows.size} rows")
+    o_ref, lse_ref = oracle.attention_rows(qb, kb, vb, wl.causal, wl.scale, rows)
+    stats = compare(o.reshape(-1, wl.d)[rows], lse.reshape(-1)[rows], o_ref, lse_ref)
+    say(f"[gpu] {wl.name} {stats}")
+    assert_parity(stats, wl.name)
+    if wl.causal:
+        np.testing.assert_array_equal(o[:, :, 0, :], bf16_bits_to_f32(vb)[:, :, 0, :])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("T", [1, 2, 31, 63, 64, 65, 127, 129, 255, 257, 1000])
+def test_ragged_and_tiny_lengths(T, causal, d):
+    qb, kb, vb = make_qkv(1, 3, T, d, seed=1000 + T + d)
+    full_check(qb, kb, vb, causal, 1.0 / math.sqrt(d), f"T={T} d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("scale", [0.01, 1.0])
+def test_other_scales(scale, d):
+    qb, kb, vb = make_qkv(2, 2, 300, d, seed=77)
+    full_check(qb, kb, vb, True, scale, f"scale={scale} d={d}")
+
+
+def test_wide_scores_force_rescaling():
+    # q and k at sigma 4 give scores with sd ~ 16 at d=64, so the running max jumps many times;
+    # v stays N(0, 1) so the output keeps the magnitude the tolerance is stated for.
+    qb, kb, _ = make_qkv(1, 4, 700, 64, seed=5, sigma=4.0)
+    _, _, vb = make_qkv(1, 4, 700, 64, seed=6)
+    full_check(qb, kb, vb, True, 0.125, "sigma4")
+    full_check(qb, kb, vb, False, 0.125, "sigma4 noncausal")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_closed_forms(causal):
+    T, d = 200, 64
+    _, kb, vb = make_qkv(1, 2, T, d, seed=21)
+    qz = np.zeros_like(kb)  # Q = 0: O is the (prefix) mean of V, LSE = ln(count)
+    o, lse = run_gpu(qz, kb, vb, causal, 0.125)
+    vf = bf16_bits_to_f32(vb).astype(np.float64)
+    if causal:
+        expect = np.cumsum(vf, axis=2) / np.arange(1, T + 1)[:, None]
+        expect_lse = np.broadcast_to(np.log(np.arange(1, T + 1)), lse.shape)
+    else:
+        expect = np.broadcast_to(vf.mean(axis=2, keepdims=True), vf.shape)
+        expect_lse = np.full(lse.shape, math.log(T))
+    assert_parity(compare(o, lse, expect, expect_lse), "Q=0")
+    # a column of ones in V: each output row of that column is the softmax row sum
+    qb, kb, _ = make_qkv(1, 2, T, d, seed=22)
+    ones = np.zeros((1, 2, T, d), dtype=np.float32)
+    ones[..., 7] = 1.0
+    o, _ = run_gpu(qb, kb, bf16_bits_from_f32(ones), causal, 0.125)
+    assert np.all(np.abs(o[..., 7] - 1.0) <= 2.0 ** -7), np.abs(o[..., 7] - 1.0).max()
+    assert np.all(o[..., :7] == 0) and np.all(o[..., 8:] == 0)
+
+
+def test_one_hot_values_expose_p():
+    T, d = 64, 64
+    qb, kb, _ = make_qkv(1, 1, T, d, seed=23)
+    eye = np.zeros((1, 1, T, d), dtype=np.float32)
+    eye[0, 0, np.arange(T), np.arange(T)] = 1.0
+    vb = bf16_bits_from_f32(eye)
+    for causal in (True, False):
+        o, lse = run_gpu(qb, kb, vb, causal, 0.125)
+        o_ref, lse_ref = oracle.attention_fwd(qb, kb, vb, causal, 0.125)
+        assert_parity(compare(o, lse, o_ref, lse_ref), "one-hot V")
+        if causal:  # masked probabilities are exactly zero
+            assert np.all(o[0, 0][np.triu(np.ones((T, T), dtype=bool), 1)] == 0.0)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_every_tile_shape(d):
+    from exact_tiled_attention_07_amd.fa import lib  # noqa: F401  (library must be loaded)
+    shapes = {64: [(128, 64, 4), (64, 64, 2), (128, 64, 2), (256, 64, 4), (256, 64, 8)],
+              128: [(128, 64, 4), (64, 64, 2)]}[d]
+    qb, kb, vb = make_qkv(2, 3, 1000, d, seed=31 + d)
+    scale = 1.0 / math.sqrt(d)
+    for causal in (True, False):
+        o_ref, lse_ref = oracle.attention_fwd(qb, kb, vb, causal, scale)
+        for bm, bn, w in shapes:
+            say(f"[gpu] tile {bm}x{bn} waves={w} d={d} causal={causal}")
+            o, lse = run_gpu_ex(qb, kb, vb, causal, scale, bm, bn, w)
+            assert_parity(compare(o, lse, o_ref, lse_ref), f"tile {bm}x{bn}x{w}")
+
+
+def test_writes_stay_inside_outputs_and_are_deterministic():
+    B, H, T, d = 2, 3, 333, 64
+    qb, kb, vb = make_qkv(B, H, T, d, seed=41)
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    n, nl = B * H * T * d, B * H * T
+    guard = 4096
+    o_big = torch.full((n + 2 * guard,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    l_big = torch.full((nl + 2 * guard,), float("nan"), dtype=torch.float32, device=DEV)
+    o = o_big[guard:guard + n].view(B, H, T, d)
+    lse = l_big[guard:guard + nl].view(B, H, T)
+    fa.fwd(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(o_big[:guard].float()).all() and torch.isnan(o_big[guard + n:].float()).all()
+    assert torch.isnan(l_big[:guard]).all() and torch.isnan(l_big[guard + nl:]).all()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    o2, lse2 = fa.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
+
+
+def test_side_stream():
+    qb, kb, vb = make_qkv(1, 4, 512, 64, seed=51)
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        o, lse = fa.fwd(q, k, v, causal=True)
+    s.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd(qb, kb, vb, True, 0.125)
+    assert_parity(compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref), "side stream")
+
+
+def test_binding_rejects_bad_tensors():
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(TypeError):
+        fa.fwd(q.float(), q, q)
+    with pytest.raises(ValueError):
+        fa.fwd(q.transpose(2, 3), q, q)
+    with pytest.raises(ValueError):
+        fa.fwd(q, q[:, :, :4], q)
+    with pytest.raises(fa.FaError):
+        fa.fwd(q[..., :32].contiguous(), q[..., :32].contiguous(), q[..., :32].contiguous())
