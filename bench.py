@@ -1,0 +1,234 @@
+"""Benchmark of the exact attention forward on one MI355X.
+
+A step is one fa_fwd call over the whole workload (all heads), inputs already resident in HBM.
+Prints one JSON line:
+  value        counted TFLOP/s of the step (2*B*H*T^2*d causal, 4*B*H*T^2*d non-causal)
+  roofline     the kernel's achieved TFLOP/s from per-launch HIP events on its own stream,
+               against the dense bf16 MFMA peak; traffic = HBM bytes per launch from rocprofv3
+               counters (when they were taken on the current kernel sources), else null
+  cpu_baseline the CPU oracle timed on the host cores on a bounded sample of the same workload
+  sweep        the same measurement at the other sequence lengths of the metric (and d=128)
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+KERNEL_SOURCES = ["exact_tiled_attention_07_amd/csrc/fa_kernel.hpp",
+                  "exact_tiled_attention_07_amd/csrc/fa_api.hip"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_hbm_traffic.txt")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic():
+    """HBM bytes per launch from the committed counter summary, if taken on these sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"kernel_source_hash:\s*(\w+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def time_workload(wl, steps, warmup, tiles=None):
+    """Returns (ms_per_step wall, avg kernel ms from per-launch events, outputs)."""
+    import torch
+
+    import exact_tiled_attention_07_amd as fa
+    from exact_tiled_attention_07_amd.inputs import to_torch_bf16
+
+    dev = torch.device("cuda:0")
+    qb, kb, vb = wl.make()
+    q, k, v = (to_torch_bf16(x, dev) for x in (qb, kb, vb))
+    del qb, kb, vb
+    o = torch.empty_like(q)
+    lse = torch.empty((wl.B, wl.H, wl.T), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)  # fa_fwd launches on this stream
+
+    def step():
+        if tiles is None:
+            fa.fwd(q, k, v, causal=wl.causal, scale=wl.scale, out=o, lse=lse, stream=stream)
+        else:
+            fa.fwd_ex(q, k, v, *tiles, causal=wl.causal, scale=wl.scale, out=o, lse=lse, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize(dev)
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+
+    # per-launch kernel duration: an event pair around each launch, on the launch stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize(dev)
+    durs = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    avg_ms = sum(durs) / len(durs)
+
+    # one cold launch: flush L2/MALL by writing 512 MiB first
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    scratch.fill_(1)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    step()
+    c1.record(stream)
+    torch.cuda.synchronize(dev)
+    cold_ms = c0.elapsed_time(c1)
+    del scratch
+    return wall_ms, avg_ms, {"median_ms": durs[len(durs) // 2], "min_ms": durs[0], "max_ms": durs[-1],
+                             "cold_ms": cold_ms}
+
+
+def cpu_baseline(wl, budget_s=20.0):
+    """Time the CPU oracle on a bounded sample of the workload (whole heads, all host cores)."""
+    import numpy as np
+
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    qb, kb, vb = wl.make()
+    d, T = wl.d, wl.T
+
+    def counted_flops(rows_per_head, heads):
+        i = np.arange(rows_per_head, dtype=np.float64)
+        per_head = (4.0 * d * (i + 1)).sum() if wl.causal else 4.0 * d * T * rows_per_head
+        return per_head * heads
+
+    # probe with one head, then take as many whole heads as fit the time budget
+    t0 = time.perf_counter()
+    oracle.attention_fwd(qb[:1, :1], kb[:1, :1], vb[:1, :1], wl.causal, wl.scale, num_threads=threads)
+    probe_s = time.perf_counter() - t0
+    n_heads_total = wl.B * wl.H
+    n_heads = max(1, min(n_heads_total, int(budget_s / max(probe_s, 1e-6))))
+    flat = [x.reshape(1, n_heads_total, T, d)[:, :n_heads] for x in (qb, kb, vb)]
+    t0 = time.perf_counter()
+    oracle.attention_fwd(*flat, wl.causal, wl.scale, num_threads=threads)
+    dt = time.perf_counter() - t0
+    fl = counted_flops(T, n_heads)
+    return {"value": float(fl / dt / 1e12), "unit": "TFLOP/s", "cores": oracle.threads_used(threads),
+            "kind": "oracle",
+            "sample": f"{n_heads} of {n_heads_total} heads of {wl.name} (all {T} rows each), "
+                      f"fp64 two-pass oracle, {dt:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="c4")
+    ap.add_argument("--tiles", default=None, help="force BMxBNxWAVES (fa_fwd_ex)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (for counter calibration)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the attention heads shard across GPUs with no exchange, so one GPU's share is the "
+              "measured unit", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from exact_tiled_attention_07_amd.inputs import WORKLOADS
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    tiles = tuple(int(x) for x in args.tiles.split("x")) if args.tiles else None
+    wl = WORKLOADS[args.workload]
+    wall_ms, kern_ms, extra = time_workload(wl, args.steps, args.warmup, tiles)
+    value = wl.flops / (wall_ms * 1e-3) / 1e12
+    achieved = wl.flops / (kern_ms * 1e-3) / 1e12
+    print(f"[bench] {wl.name}: {wall_ms:.4f} ms/step, kernel {kern_ms:.4f} ms, {value:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
+
+    sweep = {}
+    if not args.no_sweep:
+        for name in ("c3", "c5a", "c5b"):
+            if name == args.workload:
+                continue
+            w2 = WORKLOADS[name]
+            wms, kms, ex2 = time_workload(w2, max(5, args.steps // 5), max(2, args.warmup // 5), None)
+            sweep[name] = {"workload": w2.name, "ms_per_step": round(wms, 5),
+                           "tflops": round(w2.flops / (wms * 1e-3) / 1e12, 2),
+                           "kernel_tflops": round(w2.flops / (kms * 1e-3) / 1e12, 2),
+                           "pct_of_peak": round(100 * w2.flops / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
+            print(f"[bench] sweep {w2.name}: {sweep[name]}", file=sys.stderr, flush=True)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] copy calibration: 3 copies of {args.copy_calibration_mib} MiB", file=sys.stderr)
+
+    base = None
+    if not args.no_cpu_baseline:
+        base = cpu_baseline(wl)
+        print(f"[bench] cpu baseline: {base}", file=sys.stderr, flush=True)
+
+    traffic = recorded_traffic()
+    line = {
+        "metric": "causal attn fwd TFLOP/s & % of bf16 MFMA peak, B4 H12 d64, T=1K..16K",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 inputs)",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "d": wl.d,
+                   "causal": wl.causal, "input_sigma": wl.sigma, "scale": wl.scale,
+                   "tiles": args.tiles or "default"},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel_ms": round(kern_ms, 5),
+                     "flops_per_launch": wl.flops, **{k: round(v, 5) for k, v in extra.items()}},
+        "cpu_baseline": base,
+        "sweep": sweep,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,52 @@
+"""Host-side logic that needs no GPU: the bench contract and the parity tolerance helper."""
+import math
+
+import numpy as np
+import pytest
+
+import bench
+from exact_tiled_attention_07_amd.inputs import WORKLOADS, bf16_bits_from_f32, bf16_bits_to_f32
+from parity import O_TOL, bf16_ulp, compare
+
+
+def test_bench_refuses_more_than_one_gpu(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU only" in capsys.readouterr().err
+    assert bench.main(["--gpus", "8", "--steps", "1"]) == 2
+
+
+def test_bench_traffic_record_matches_sources():
+    # the committed counter summary is used only while the kernel sources are unchanged
+    t = bench.recorded_traffic()
+    text = open(bench.TRAFFIC_FILE).read() if __import__("os").path.exists(bench.TRAFFIC_FILE) else ""
+    if bench.kernel_source_hash() in text:
+        assert t is not None and t > 0
+    else:
+        assert t is None
+
+
+def test_bench_cpu_baseline_small():
+    r = bench.cpu_baseline(WORKLOADS["c1"], budget_s=1.0)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["cores"] >= 1
+    assert r["value"] > 0 and "heads of c1" in r["sample"]
+
+
+def test_bf16_ulp_is_the_spacing_of_bf16():
+    x = np.array([1.0, 1.5, 2.0, 3.99, 4.0, 7.5, 8.0, 0.75, -5.0])
+    ulp = bf16_ulp(x)
+    # the next bf16 value above |x| (for x on the bf16 grid) is |x| + ulp
+    for xi, ui in zip(np.abs(x), ulp):
+        b = bf16_bits_from_f32(np.float32(xi))
+        nxt = bf16_bits_to_f32(np.uint16(int(b) + 1))
+        if bf16_bits_to_f32(b) == np.float32(xi):
+            assert nxt - xi == pytest.approx(ui)
+    assert ulp[0] == 2.0 ** -7 and ulp[4] == 2.0 ** -5 and ulp[6] == 2.0 ** -4
+
+
+def test_tolerance_reading():
+    ref = np.array([0.5, 3.0, 5.0, 5.0, 1.0])
+    gpu = np.array([0.5 + 0.014, 3.0 + 0.0155, 5.0 + 0.031, 5.0 + 0.032, 1.0 - 0.016])
+    s = compare(gpu, np.zeros(1), ref, np.zeros(1))
+    # 0.014 literal; 0.0155 <= ulp(3)=2^-6; 0.031 <= ulp(5)=2^-5; 0.032 > 2^-5 fails; 0.016 at |1| fails
+    assert s["n_ulp_clause"] == 2 and s["n_fail_o"] == 2
+    assert math.isclose(O_TOL, 1.5e-2)
