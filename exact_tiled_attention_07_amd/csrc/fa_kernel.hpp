@@ -5,15 +5,19 @@
 //   - one workgroup owns one Q block of one (batch, head) and walks the K/V blocks; Q blocks never
 //     communicate (learn-llm.fim.ai "手写 FlashAttention：拆开 SDPA 这个黑盒", STEP 3);
 //   - per K/V block: scores on chip, running row max m and l = sum exp(x - m), and the output
-//     accumulator rescaled by alpha = exp(m_old - m_new) when the max grows (same page, STEP 2);
+//     accumulator rescaled by alpha = exp(m_old - m_new) (same page, STEP 2); alpha is applied on
+//     every block (it is exactly 1 when the max did not grow), which keeps the loop branch-free;
 //   - the division by l happens once, after the last block (same page, STEP 2, the note on
 //     FlashAttention-2 moving the divide to the end; cnblogs "内核案例研究：Flash Attention",
 //     section "块稀疏注意力 V2 和 V3", item 3);
 //   - exp2 with log2(e) folded into the softmax scale, so m and l live in base 2 and the base
 //     cancels in acc / l (learn-llm page, STEP 4, note on exp2 and 1.4427);
-//   - causal blocks that lie wholly above the diagonal are skipped, and only blocks that touch the
-//     diagonal (or the ragged end of the sequence) are masked element by element (STEP 3 legend;
-//     STEP 5 note contrasting per-block masking with separate diagonal handling);
+//   - causal blocks that lie wholly above the diagonal are never loaded, and only blocks that touch
+//     the diagonal (or the ragged end of the sequence) are masked element by element (STEP 3
+//     legend; STEP 5 note contrasting per-block masking with separate diagonal handling);
+//   - the softmax of one block runs while the matrix unit computes the next block's scores, the
+//     overlap of non-matrix work with matrix work that the cnblogs page describes for its third
+//     version ("最近在 V3 版本中");
 //   - the per-row logsumexp is written for a backward pass (STEP 4, note on training).
 //
 // gfx950 mapping (measured on the device, not taken from the pages):
@@ -25,12 +29,19 @@
 //   - The output is computed transposed too, O^T = V^T P^T: the P^T operand is exactly the S^T
 //     accumulator layout (after exp and bf16 rounding), and the rescale factor is per lane.
 //   - V^T comes from the row-major V tile through ds_read_b64_tr_b16 (a transposing LDS read).
-//   - K/V tiles go HBM -> LDS with global_load_lds_dwordx4 (no register staging), double
-//     buffered, 16-byte chunks XOR-swizzled per row against LDS bank conflicts.
+//   - K/V tiles go HBM -> LDS with global_load_lds_dwordx4 (no register staging); K is fetched two
+//     tiles ahead and V one tile ahead into separate double buffers, 16-byte chunks XOR-swizzled
+//     per row against LDS bank conflicts.
+//   - Each wave is software-pipelined: in step j its MFMA "slots" first compute S(j+1) = K(j+1) Q^T
+//     and then O += V(j)^T P(j)^T, while the VALU work of the softmax of tile j (and the row max
+//     of S(j+1)) is spread over those slots. LDS fragments are read a few slots ahead with
+//     explicit lgkmcnt waits.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace fa {
 
@@ -39,13 +50,9 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// The running max may lag the true max by up to this much (base-2 units) before the accumulator is
-// rescaled. Any stabiliser gives the same exact result because it cancels in acc / l; this bound
-// keeps every exp2 argument <= 8, so p <= 256 and l <= 256 * T stays far from fp32 overflow.
-constexpr float kRescaleSlack = 8.0f;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -61,20 +68,41 @@ struct Cfg {
   static constexpr int ROW_BYTES = D * 2;           // one bf16 row of K or V
   static constexpr int CHUNKS = D / 8;              // 16-byte chunks per row
   static constexpr int TILE_BYTES = BN * ROW_BYTES; // one K (or V) tile
-  static constexpr int LDS_BYTES = 4 * TILE_BYTES;  // K and V, two buffers each
+  static constexpr int LDS_BYTES = 4 * TILE_BYTES;  // K0 K1 V0 V1
   static constexpr int LOADS = TILE_BYTES / (16 * THREADS);  // 16-byte loads per lane per tile
   static constexpr int KSTEPS = D / 16;             // k-steps of the score MFMA
   static constexpr int KB = BN / 32;                // 32-key blocks per tile
   static constexpr int CB = D / 32;                 // 32-channel blocks of the output
   static constexpr int PT = BN / 16;                // k-steps of the P.V MFMA
+  static constexpr int NS_QK = KSTEPS * KB;         // score MFMA slots per tile (QB MFMAs each)
+  static constexpr int NS_PV = PT * CB;             // P.V MFMA slots per tile (QB MFMAs each)
+  static constexpr int NS = NS_QK + NS_PV;
+  static constexpr int NPAIRS = KB * 8;             // score pairs per lane per 32-query block
+  static constexpr int PD = 3;                      // LDS fragment prefetch distance, in slots
+  // exp pairs are spread over slots [0, EXP_WINDOW); pair p must be done before the P.V slots of
+  // its k-step p/4 start.
+  static constexpr int EXP_WINDOW = NS_QK + (PT - 1) * CB;
+  // the mask and row max of the next tile are spread over slots [MAX_FIRST, NS)
+  static constexpr int MAX_FIRST = NS_QK + 2 < NS - 1 ? NS_QK + 2 : NS - 1;
+  static constexpr int KBUF0 = 0, KBUF1 = TILE_BYTES, VBUF0 = 2 * TILE_BYTES, VBUF1 = 3 * TILE_BYTES;
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(BN % 32 == 0 && BN >= 32, "tile keys");
   static_assert(LOADS >= 1 && LOADS * 16 * THREADS == TILE_BYTES, "tile load split");
+  static_assert(LDS_BYTES <= 65536, "LDS immediate offsets are 16-bit");
 };
+
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // Physical 16-byte chunk of logical chunk c in LDS row r. An involution (XOR), so the same
 // function maps physical back to logical. With 128-byte rows (d=64) two consecutive rows share a
 // bank half, so the key is r/2; with 256-byte rows (d=128) every row starts on bank 0, so it is r.
+// Adding a multiple of 16 to r leaves the key unchanged for both.
 template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
   return D == 64 ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15));
@@ -91,16 +119,32 @@ __device__ __forceinline__ float wave_sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// Sum of the two bf16 halves of a packed pair, added to acc in fp32 (v_dot2c_f32_bf16 with 1, 1).
-__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
-}
-
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   f32x2 f = {a, b};
   bf16x2 h = __builtin_convertvector(f, bf16x2);  // v_cvt_pk_bf16_f32, round to nearest even
   return __builtin_bit_cast(uint32_t, h);
+}
+
+// LDS reads as inline asm. The compiler cannot see which LDS bytes a transposing read touches, so
+// with the builtin it would wait for every in-flight HBM->LDS copy (including the one filling the
+// other buffer) before the read. Here the reads are issued early and waited for explicitly with
+// lgkm_wait<N>(): LDS returns in order, so "at most N outstanding" means all but the last N done.
+template <int OFF>
+__device__ __forceinline__ void lds_read_b128(bf16x8& dst, uint32_t addr) {
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void lds_read_tr16(s16x4& dst, uint32_t addr) {
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(OFF));
+}
+template <int N>
+__device__ __forceinline__ void lgkm_wait() {
+  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
+}
+template <class T>
+__device__ __forceinline__ void after_wait(T& x) {
+  asm volatile("" : "+v"(x));  // orders uses of x after the preceding wait
 }
 
 // Map the flat workgroup id to (Q block, batch*head). Workgroups are handed to the 8 XCDs round
@@ -120,13 +164,27 @@ __device__ __forceinline__ void map_block(int bid, int nq, int BH, int& qblk, in
   qblk = CAUSAL ? (nq - 1 - rank) : rank;
 }
 
+// Number of LDS reads a step slot issues: one K read for a score slot, two V reads otherwise.
+template <int NS_QK>
+constexpr int slot_reads(int b) {
+  return b < NS_QK ? 1 : 2;
+}
+template <int NS_QK, int NS>
+constexpr int reads_between(int first, int last) {
+  int c = 0;
+  for (int x = first; x <= last && x < NS; ++x) c += slot_reads<NS_QK>(x);
+  return c;
+}
+
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int T, int nq, int BH, float scale_log2) {
   constexpr int D = C::D, QB = C::QB, NW = C::NW, BN = C::BN, BM = C::BM;
-  constexpr int KB = C::KB, CB = C::CB, PT = C::PT, KSTEPS = C::KSTEPS;
+  constexpr int KB = C::KB, CB = C::CB, PT = C::PT, KSTEPS = C::KSTEPS, RB = C::ROW_BYTES;
+  constexpr int NS_QK = C::NS_QK, NS = C::NS, PD = C::PD;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -140,55 +198,52 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   const int64_t head_off = (int64_t)bh * T * D;
   const char* kg = reinterpret_cast<const char*>(k + head_off);
   const char* vg = reinterpret_cast<const char*>(v + head_off);
+  const int qw0 = q0 + 32 * QB * w;  // first query of this wave
 
-  // Number of K/V tiles this workgroup needs: up to the diagonal when causal.
+  // K/V tiles this workgroup needs: up to the diagonal when causal (tiles above it are never
+  // touched), all of them otherwise. The last one reaches past T only for a ragged end.
   const int kv_end = C::CAUSAL ? min(q0 + BM, T) : T;
-  const int ntiles = (kv_end + BN - 1) / BN;
+  const int n_tiles = (kv_end + BN - 1) / BN;
+  const bool tail_ragged = n_tiles * BN > T;
 
-  // ---- K/V tile loads, HBM -> LDS directly. Rows past T are clamped to row T-1 (always in
-  // bounds); their scores are masked and their V rows are zeroed before use.
-  auto issue_tile = [&](int j, int buf) {
-    const int kt0 = j * BN;
-    char* kl = smem + buf * 2 * C::TILE_BYTES;
-    char* vl = kl + C::TILE_BYTES;
+  // ---- HBM -> LDS copies of one K or V tile. Lane `lane` of load i fills 16 bytes of the 1 KiB
+  // LDS region (i*NW + w); it fetches the logical chunk that the swizzle puts there. Rows past T
+  // are clamped to row T-1 (always in bounds); their scores are masked and their V rows zeroed.
+  int dma_row[C::LOADS], dma_col[C::LOADS];
+#pragma unroll
+  for (int i = 0; i < C::LOADS; ++i) {
+    const int lofs = (i * NW + w) * 1024 + lane * 16;
+    dma_row[i] = lofs / RB;
+    dma_col[i] = swz<D>(dma_row[i], (lofs % RB) >> 4) * 16;
+  }
+  auto dma = [&](const char* g, int tile, int buf_off) {
+    const int kt0 = tile * BN;
 #pragma unroll
     for (int i = 0; i < C::LOADS; ++i) {
-      const int region = i * NW + w;                 // 1 KiB of LDS per wave instruction
-      const int lofs = region * 1024 + lane * 16;    // byte offset inside the tile
-      const int r = lofs / C::ROW_BYTES;
-      const int pc = (lofs % C::ROW_BYTES) >> 4;
-      const int lc = swz<D>(r, pc);
-      const int grow = min(kt0 + r, T - 1);
-      const int64_t gofs = (int64_t)grow * C::ROW_BYTES + lc * 16;
+      const uint32_t gofs = (uint32_t)(min(kt0 + dma_row[i], T - 1) * RB + dma_col[i]);
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(kg + gofs),
-          (__attribute__((address_space(3))) void*)(kl + region * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(vg + gofs),
-          (__attribute__((address_space(3))) void*)(vl + region * 1024), 16, 0, 0);
+          (const __attribute__((address_space(1))) void*)(g + gofs),
+          (__attribute__((address_space(3))) void*)(smem + buf_off + (i * NW + w) * 1024), 16, 0, 0);
     }
   };
   // Zero the V rows at or past T of a ragged last tile, so a clamped copy of row T-1 can never
-  // reach the output (0 * p stays 0 even for non-finite p; p is 0 there anyway).
-  auto zero_v_tail = [&](int j, int buf) {
-    const int kt0 = j * BN;
-    const int first = T - kt0;  // first row to clear, 0 < first < BN
-    char* vl = smem + buf * 2 * C::TILE_BYTES + C::TILE_BYTES;
+  // reach the output (their weights are 0; a non-finite input row would still give 0 * inf).
+  auto zero_v_tail = [&](int buf_off) {
+    const int first = T - (n_tiles - 1) * BN;  // first row to clear, 0 < first < BN
+    char* vl = smem + buf_off;
     for (int idx = tid; idx < (BN - first) * C::CHUNKS; idx += C::THREADS) {
       const int r = first + idx / C::CHUNKS;
-      const int c = idx % C::CHUNKS;
-      *reinterpret_cast<u32x4*>(vl + r * C::ROW_BYTES + c * 16) = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(vl + r * RB + (idx % C::CHUNKS) * 16) = u32x4{0u, 0u, 0u, 0u};
     }
   };
-  // The last tile reaches past T only for a ragged sequence end.
-  const bool tail_ragged = ntiles * BN > T;
 
-  issue_tile(0, 0);
+  dma(kg, 0, C::KBUF0);
+  dma(vg, 0, C::VBUF0);
+  if (n_tiles > 1) dma(kg, 1, C::KBUF1);
 
   // ---- Q fragments straight into registers: B operand of S^T = K Q^T. Lane (n, hf) holds
-  // query row q0 + 32*(QB*w + qb) + n, channels 16*s + 8*hf .. +7.
+  // query row qw0 + 32*qb + n, channels 16*s + 8*hf .. +7.
   bf16x8 qf[QB][KSTEPS];
-  const int qw0 = q0 + 32 * QB * w;  // first query of this wave
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = min(qw0 + 32 * qb + n, T - 1);
@@ -197,168 +252,301 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     for (int s = 0; s < KSTEPS; ++s) qf[qb][s] = src[2 * s + hf];
   }
 
-  // Per query row (this lane's half of the keys): running max m (base 2, scaled), the fp32 sum
-  // l of the exponentials (for the logsumexp) and the sum w of the same weights after rounding to
-  // bf16, i.e. of exactly the weights that enter P.V. O is normalised by w, so the rounding of a
-  // dominant weight cancels between numerator and denominator instead of scaling its V row.
+  // ---- per-lane LDS byte addresses of the MFMA fragments (the buffer and the k-step / key block
+  // parts are compile-time immediates).
+  // K fragment (kb, s): row 32*kb + n, channels 16*s + 8*hf .. +7.
+  uint32_t k_addr[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) k_addr[s] = lds0 + n * RB + swz<D>(n, 2 * s + hf) * 16;
+  // V^T fragment (t, cb): lane l (group g = l/16, i = l%16) holds V^T row c(cb, l%32) at the 8
+  // keys of its P^T slots, via two transposing reads of 4 keys each. Source lane i of a group
+  // reads V row (16*t + 4*(g/2) + i/4 [+ 8]) at 4 channels starting at the column below.
+  uint32_t v_addr[CB][2];
+  {
+    const int grp = lane >> 4, gi = lane & 15;
+    const int ga = grp & 1, gh = grp >> 1;
+    const int e_src = gi >> 2, q_src = gi & 3;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) {
+      const int col = (D / 2) * (q_src & 1) + 16 * cb + 4 * (2 * ga + (q_src >> 1));
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) {
+        const int r = 4 * gh + e_src + 8 * rr;
+        v_addr[cb][rr] = lds0 + r * RB + swz<D>(r, col >> 3) * 16 + (col & 7) * 2;
+      }
+    }
+  }
+
+  // Per query row: the exact running max m (base 2, scaled; the same in both halves of the wave),
+  // the fp32 sum l of this lane's half of the exponentials, and the factor alpha = exp2(m_old -
+  // m_new) still to be applied to acc and l before the next block is added. Because m is the
+  // exact max, the largest weight of a row is exactly 1 and needs no rounding in bf16.
   f32x16 acc[CB][QB];
-  float m_run[QB], l_run[QB], w_run[QB];
+  float m_run[QB], l_run[QB], alpha[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -__builtin_inff();
     l_run[qb] = 0.0f;
-    w_run[qb] = 0.0f;
+    alpha[qb] = 1.0f;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) acc[cb][qb] = f32x16{};
   }
+  f32x16 sa[KB][QB], sb[KB][QB];  // scores of the current and the next tile (ping-pong)
+  u32x4 pf[QB][PT];               // bf16 P of the current tile, B operand layout of P.V
 
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tail_ragged && ntiles == 1) {
-    zero_v_tail(0, 0);
-    __syncthreads();
-  }
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) issue_tile(j + 1, buf ^ 1);
-
-    const int kt0 = j * BN;
-    const bool active = !C::CAUSAL || kt0 <= qw0 + 32 * QB - 1;
-    if (active) {
-      const char* kl = smem + buf * 2 * C::TILE_BYTES;
-      const char* vl = kl + C::TILE_BYTES;
-
-      // ---- S^T = K Q^T: lane (n, hf) gets query column n; register r of block kb is key
-      // kt0 + 32*kb + 8*(r/4) + 4*hf + r%4.
-      f32x16 st[KB][QB];
+  // ---- score-tile helpers -----------------------------------------------------------------
+  // Mask tile `tile` of scores in place: key > query (causal) or key >= T become -inf.
+  auto mask_tile = [&](f32x16 (&s)[KB][QB], int tile) {
+    const int kt0 = tile * BN;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int qi = qw0 + 32 * qb + n;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) st[kb][qb] = f32x16{};
-#pragma unroll
-      for (int s = 0; s < KSTEPS; ++s) {
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          const int r = 32 * kb + n;
-          const bf16x8 kfrag =
-              *reinterpret_cast<const bf16x8*>(kl + r * C::ROW_BYTES + swz<D>(r, 2 * s + hf) * 16);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            st[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfrag, qf[qb][s], st[kb][qb], 0, 0, 0);
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const bool visible = (key < T) && (!C::CAUSAL || key <= qi);
+          s[kb][qb][r] = visible ? s[kb][qb][r] : -__builtin_inff();
         }
-      }
-
-      // ---- mask: only tiles that reach past this wave's first query (causal) or past T.
-      const bool need_mask = (C::CAUSAL && kt0 + BN - 1 > qw0) || (kt0 + BN > T);
-      if (need_mask) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int qi = qw0 + 32 * qb + n;
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = kt0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-              const bool visible = (key < T) && (!C::CAUSAL || key <= qi);
-              st[kb][qb][r] = visible ? st[kb][qb][r] : -__builtin_inff();
-            }
-        }
-      }
-
-      // ---- online softmax (base 2) and P in bf16, laid out as the B operand of O^T += V^T P^T.
-      bf16x8 pf[QB][PT];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[kb][qb][r]);
-        mx = wave_max_halves(mx) * scale_log2;  // scale_log2 > 0, so scaling keeps the max
-        // Rescale only when some row's max rose by more than the slack; otherwise the previous
-        // max keeps serving as the stabiliser (exact: it cancels in acc / l).
-        const bool grow = mx > m_run[qb] + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-          const float m_new = fmaxf(m_run[qb], mx);
-          const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-          l_run[qb] *= alpha;
-          w_run[qb] *= alpha;
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) acc[cb][qb] *= alpha;
-          m_run[qb] = m_new;
-        }
-        const float neg_m = -m_run[qb];
-        float lsum0 = 0.0f, lsum1 = 0.0f, wsum = 0.0f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            uint32_t pk[4];
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-              const int r = 8 * half + e;
-              const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][qb][r], scale_log2, neg_m));
-              const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[kb][qb][r + 1], scale_log2, neg_m));
-              lsum0 += p0;
-              lsum1 += p1;
-              pk[e >> 1] = pack_bf16x2(p0, p1);
-              wsum = add_bf16_pair(pk[e >> 1], wsum);
-            }
-            u32x4 pv = {pk[0], pk[1], pk[2], pk[3]};
-            pf[qb][2 * kb + half] = __builtin_bit_cast(bf16x8, pv);
-          }
-        }
-        l_run[qb] += lsum0 + lsum1;
-        w_run[qb] += wsum;
-      }
-
-      // ---- O^T += V^T P^T. A operand: lane l (group g = l/16, i = l%16) must hold V^T row
-      // c(cb, l%32) at the 8 keys of its P^T slots. Two transposing reads, 4 keys each: source lane
-      // i of a group reads V row (key base + i/4), 4 channels starting at the column below.
-      const int grp = lane >> 4, gi = lane & 15;
-      const int ga = grp & 1, gh = grp >> 1;
-      const int e_src = gi >> 2, q_src = gi & 3;
-#pragma unroll
-      for (int t = 0; t < PT; ++t) {
-        const int kb = t >> 1, u = t & 1;
-        const int r1 = 32 * kb + 16 * u + 4 * gh + e_src;  // key row of the first read
-        const int r2 = r1 + 8;                              // and of the second
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const int col = (D / 2) * (q_src & 1) + 16 * cb + 4 * (2 * ga + (q_src >> 1));
-          const int chunk = col >> 3, within = (col & 7) * 2;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(vl + r1 * C::ROW_BYTES + swz<D>(r1, chunk) * 16 + within));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(vl + r2 * C::ROW_BYTES + swz<D>(r2, chunk) * 16 + within));
-          typedef short s16x8 __attribute__((ext_vector_type(8)));
-          const s16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          const bf16x8 vfrag = __builtin_bit_cast(bf16x8, both);
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            acc[cb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag, pf[qb][t], acc[cb][qb], 0, 0, 0);
-        }
-      }
     }
+  };
+  auto needs_mask = [&](int tile) {
+    const int kt0 = tile * BN;
+    return (C::CAUSAL && kt0 + BN - 1 > qw0) || (kt0 + BN > T);
+  };
+  // One pair of scores -> exp2, fp32 row sum, packed bf16 P. Pair p covers registers 2*(p%8), +1
+  // of key block p/8, i.e. element p%4 of P^T k-step p/4.
+  auto exp_pair = [&](f32x16 (&s)[KB][QB], int qb, int p, float neg_m, float& lsum) {
+    const int kb = p >> 3, r = (p & 7) * 2;
+    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], scale_log2, neg_m));
+    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r + 1], scale_log2, neg_m));
+    lsum += p0 + p1;
+    uint32_t pk = pack_bf16x2(p0, p1);
+    // keep this pair's work in the slot it was placed in (the optimizer would otherwise sink it
+    // towards its P.V use, past the slots whose MFMAs it is meant to overlap)
+    asm volatile("" : "+v"(pk), "+v"(lsum));
+    pf[qb][p >> 2][p & 3] = pk;
+  };
+  // Apply the pending rescale to registers [r0, r1) of every output block of query block qb.
+  auto rescale_chunk = [&](int qb, int r0, int r1) {
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = r0; r < r1; ++r) acc[cb][qb][r] *= alpha[qb];
+  };
+  // Row max (raw scores) over registers [r0, r1) of every key block.
+  auto max_chunk = [&](f32x16 (&s)[KB][QB], int qb, int r0, int r1, float& mx) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = r0; r < r1; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+  };
+  // Online-softmax max update with the finished row max mx (raw scores) of the next tile; the
+  // factor for acc and l is applied while that tile is processed. A fully masked row chunk has
+  // mx = -inf and leaves m unchanged (alpha = 1).
+  auto update_max = [&](float (&mx)[QB]) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const float m_new = fmaxf(m_run[qb], wave_max_halves(mx[qb]) * scale_log2);  // scale_log2 > 0
+      alpha[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+      m_run[qb] = m_new;
+    }
+  };
+  auto pv_mfma = [&](int cb, int t, s16x4 lo, s16x4 hi) {
+    const bf16x8 vfrag =
+        __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      acc[cb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag, __builtin_bit_cast(bf16x8, pf[qb][t]),
+                                                           acc[cb][qb], 0, 0, 0);
+  };
 
-    // Tile j+1 has landed in LDS for this wave; the barrier makes it (and the end of every wave's
-    // reads of tile j) visible to all waves.
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  // ---- prologue: tiles 0 (K, V) and 1 (K) in LDS; S(0) = K(0) Q^T; first row max.
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tail_ragged && n_tiles == 1) {
+    zero_v_tail(C::VBUF0);
     __syncthreads();
-    if (tail_ragged && j + 2 == ntiles) {
-      zero_v_tail(j + 1, buf ^ 1);
-      __syncthreads();
+  }
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) sa[kb][qb] = f32x16{};
+  static_for<0, KSTEPS>([&](auto s_) {
+    constexpr int s = decltype(s_)::value;
+    bf16x8 kf[KB];
+    static_for<0, KB>([&](auto kb_) {
+      constexpr int kb = decltype(kb_)::value;
+      lds_read_b128<C::KBUF0 + kb * 32 * RB>(kf[kb], k_addr[s]);
+    });
+    lgkm_wait<0>();
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      after_wait(kf[kb]);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb)
+        sa[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb], qf[qb][s], sa[kb][qb], 0, 0, 0);
     }
+  });
+  __syncthreads();  // every wave has read K(0) before K(2) is copied into its buffer
+  if (needs_mask(0)) mask_tile(sa, 0);
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    float mx = -__builtin_inff();
+    max_chunk(sa, qb, 0, 16, mx);
+    m_run[qb] = wave_max_halves(mx) * scale_log2;  // key 0 is visible to every row: finite
   }
 
-  // ---- epilogue: O = acc / w, rounded once to bf16; LSE = ln2 * (m + log2 l).
+  // ---- one pipelined step: softmax + P.V of tile j (scores in s_cur, V in buffer VR) while the
+  // scores of tile j+1 (K in buffer KR) go into s_nxt. Copies K(j+2) -> KW and V(j+1) -> VW.
+  auto step = [&](auto kr_, auto vr_, auto kw_, auto vw_, int j, f32x16 (&s_cur)[KB][QB],
+                  f32x16 (&s_nxt)[KB][QB]) {
+    constexpr int KR = decltype(kr_)::value, VR = decltype(vr_)::value;
+    constexpr int KW = decltype(kw_)::value, VW = decltype(vw_)::value;
+    dma(kg, min(j + 2, n_tiles - 1), KW);  // past the end: a harmless re-copy of the last tile
+    dma(vg, j + 1, VW);
+
+    float neg_m[QB], lsum[QB], mx[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      neg_m[qb] = -m_run[qb];
+      l_run[qb] *= alpha[qb];
+      lsum[qb] = 0.0f;
+      mx[qb] = -__builtin_inff();
+    }
+    const bool mask_next = needs_mask(j + 1);
+
+    // LDS fragment of slot b: one K read (score slots) or two transposing V reads (P.V slots).
+    bf16x8 kfr[NS_QK];
+    s16x4 vfr[C::NS_PV][2];
+    auto issue = [&](auto b_) {
+      constexpr int b = decltype(b_)::value;
+      if constexpr (b < NS_QK) {
+        constexpr int s = b / KB, kb = b % KB;
+        lds_read_b128<KR + kb * 32 * RB>(kfr[b], k_addr[s]);
+      } else {
+        constexpr int t = (b - NS_QK) / CB, cb = (b - NS_QK) % CB;
+        lds_read_tr16<VR + t * 16 * RB>(vfr[b - NS_QK][0], v_addr[cb][0]);
+        lds_read_tr16<VR + t * 16 * RB>(vfr[b - NS_QK][1], v_addr[cb][1]);
+      }
+    };
+    static_for<0, PD>([&](auto b_) { issue(b_); });
+
+    static_for<0, NS>([&](auto b_) {
+      constexpr int b = decltype(b_)::value;
+      // prefetch slot b+PD, then wait until only the reads of slots b+1 .. b+PD are outstanding
+      if constexpr (b + PD < NS) issue(std::integral_constant<int, b + PD>{});
+      lgkm_wait<reads_between<NS_QK, NS>(b + 1, b + PD)>();
+      if constexpr (b < NS_QK) {
+        constexpr int s = b / KB, kb = b % KB;
+        after_wait(kfr[b]);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s_nxt[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              kfr[b], qf[qb][s], s == 0 ? f32x16{} : s_nxt[kb][qb], 0, 0, 0);
+      } else {
+        constexpr int t = (b - NS_QK) / CB, cb = (b - NS_QK) % CB;
+        after_wait(vfr[b - NS_QK][0]);
+        after_wait(vfr[b - NS_QK][1]);
+        pv_mfma(cb, t, vfr[b - NS_QK][0], vfr[b - NS_QK][1]);
+      }
+      // VALU work of this slot: the exp pairs assigned to it ...
+      if constexpr (b < C::EXP_WINDOW) {
+        constexpr int p_lo = (b * C::NPAIRS + C::EXP_WINDOW - 1) / C::EXP_WINDOW;
+        constexpr int p_hi = ((b + 1) * C::NPAIRS + C::EXP_WINDOW - 1) / C::EXP_WINDOW;
+        static_for<p_lo, (p_hi < C::NPAIRS ? p_hi : C::NPAIRS)>([&](auto p_) {
+          constexpr int p = decltype(p_)::value;
+          static_assert(NS_QK + (p / 4) * CB > b, "exp pair scheduled after its P.V slot");
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) exp_pair(s_cur, qb, p, neg_m[qb], lsum[qb]);
+        });
+      }
+      // ... the pending rescale of acc, spread over the score slots (before any P.V slot) ...
+      if constexpr (b < NS_QK) {
+        constexpr int r0 = b * 16 / NS_QK, r1 = (b + 1) * 16 / NS_QK;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) rescale_chunk(qb, r0, r1);
+      }
+      // ... and, once the next scores are complete, their mask and a chunk of their row max.
+      if constexpr (b == C::MAX_FIRST) {
+        if (mask_next) mask_tile(s_nxt, j + 1);
+      }
+      if constexpr (b >= C::MAX_FIRST) {
+        constexpr int nmax = NS - C::MAX_FIRST;
+        constexpr int r0 = (b - C::MAX_FIRST) * 16 / nmax, r1 = (b - C::MAX_FIRST + 1) * 16 / nmax;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) max_chunk(s_nxt, qb, r0, r1, mx[qb]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) l_run[qb] += lsum[qb];
+    update_max(mx);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // K(j+2), V(j+1) landed; every wave is done with K(j+1) and V(j)
+    if (tail_ragged && j + 2 == n_tiles) {
+      zero_v_tail(VW);
+      __syncthreads();
+    }
+  };
+
+  // ---- last tile: softmax and P.V only.
+  auto last_step = [&](auto vr_, f32x16 (&s_cur)[KB][QB]) {
+    constexpr int VR = decltype(vr_)::value;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float lsum = 0.0f;
+      const float neg_m = -m_run[qb];
+      rescale_chunk(qb, 0, 16);
+#pragma unroll
+      for (int p = 0; p < C::NPAIRS; ++p) exp_pair(s_cur, qb, p, neg_m, lsum);
+      l_run[qb] = l_run[qb] * alpha[qb] + lsum;
+    }
+    static_for<0, PT>([&](auto t_) {
+      constexpr int t = decltype(t_)::value;
+      s16x4 lo[CB], hi[CB];
+      static_for<0, CB>([&](auto cb_) {
+        constexpr int cb = decltype(cb_)::value;
+        lds_read_tr16<VR + t * 16 * RB>(lo[cb], v_addr[cb][0]);
+        lds_read_tr16<VR + t * 16 * RB>(hi[cb], v_addr[cb][1]);
+      });
+      lgkm_wait<0>();
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        after_wait(lo[cb]);
+        after_wait(hi[cb]);
+        pv_mfma(cb, t, lo[cb], hi[cb]);
+      }
+    });
+  };
+
+  using K0 = std::integral_constant<int, C::KBUF0>;
+  using K1 = std::integral_constant<int, C::KBUF1>;
+  using V0 = std::integral_constant<int, C::VBUF0>;
+  using V1 = std::integral_constant<int, C::VBUF1>;
+  // Tile j's V sits in buffer j%2 and tile j+1's K in buffer (j+1)%2; unrolled by two so every
+  // buffer offset is an immediate and the score ping-pong needs no register copies.
+  for (int j = 0;; j += 2) {
+    if (j + 1 >= n_tiles) {
+      last_step(V0{}, sa);
+      break;
+    }
+    step(K1{}, V0{}, K0{}, V1{}, j, sa, sb);
+    if (j + 2 >= n_tiles) {
+      last_step(V1{}, sb);
+      break;
+    }
+    step(K0{}, V1{}, K1{}, V0{}, j + 1, sb, sa);
+  }
+
+  // ---- epilogue: O = acc / l, rounded once to bf16; LSE = ln2 * (m + log2 l).
   // Lane (n, hf) of channel block cb holds channels (D/2)*hf + 16*cb + r, r = 0..15, in order.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qw0 + 32 * qb + n;
     const float l_tot = wave_sum_halves(l_run[qb]);
-    const float inv = 1.0f / wave_sum_halves(w_run[qb]);
+    const float inv = 1.0f / l_tot;
     if (row < T) {
       char* orow = reinterpret_cast<char*>(o + head_off + (int64_t)row * D);
 #pragma unroll
