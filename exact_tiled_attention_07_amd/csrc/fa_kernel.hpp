@@ -34,8 +34,7 @@
 //     per row against LDS bank conflicts.
 //   - Each wave is software-pipelined: in step j its MFMA "slots" first compute S(j+1) = K(j+1) Q^T
 //     and then O += V(j)^T P(j)^T, while the VALU work of the softmax of tile j (and the row max
-//     of S(j+1)) is spread over those slots. LDS fragments are read a few slots ahead with
-//     explicit lgkmcnt waits.
+//     of S(j+1)) is spread over those slots. LDS fragments are read a few slots ahead.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -99,13 +98,23 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// Physical 16-byte chunk of logical chunk c in LDS row r. An involution (XOR), so the same
-// function maps physical back to logical. With 128-byte rows (d=64) two consecutive rows share a
-// bank half, so the key is r/2; with 256-byte rows (d=128) every row starts on bank 0, so it is r.
-// Adding a multiple of 16 to r leaves the key unchanged for both.
+// Physical 16-byte chunk of logical chunk c in LDS row r: c XOR a per-row key (an involution, so
+// the same function maps physical back to logical). The key is a bit permutation of r/2 (128-byte
+// rows, d=64: two consecutive rows fill the two bank halves) or of r (256-byte rows, d=128). It is
+// chosen so that (a) the 16 lanes of a K read (16 consecutive rows, one chunk) hit distinct banks,
+// and (b) the four rows of each 16-lane group of a transposing V read, each read at the chunk set
+// {c, c^1, c^4, c^5} (d=64) or {c, c^1, c^8, c^9} (d=128), land in disjoint banks: the low bits of
+// the row pick key bits that those chunk sets do not cover. Adding a multiple of 16 to r leaves the
+// key unchanged.
 template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
-  return D == 64 ? (c ^ ((r >> 1) & 7)) : (c ^ (r & 15));
+  if constexpr (D == 64) {
+    const int g = (r >> 1) & 7;
+    return c ^ (((g & 1) << 1) | ((g >> 1) & 1) | (g & 4));
+  } else {
+    const int x = r & 15;
+    return c ^ (((x & 3) << 1) | ((x >> 2) & 1) | (x & 8));
+  }
 }
 
 __device__ __forceinline__ float wave_max_halves(float x) {
@@ -125,27 +134,36 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// LDS reads as inline asm. The compiler cannot see which LDS bytes a transposing read touches, so
-// with the builtin it would wait for every in-flight HBM->LDS copy (including the one filling the
-// other buffer) before the read. Here the reads are issued early and waited for explicitly with
-// lgkm_wait<N>(): LDS returns in order, so "at most N outstanding" means all but the last N done.
-template <int OFF>
-__device__ __forceinline__ void lds_read_b128(bf16x8& dst, uint32_t addr) {
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(OFF));
+// HBM -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4) as inline asm: LDS bytes
+// [lds_addr + 16*lane, +16) <- global bytes [base + voff, +16). If the compiler saw these copies it
+// would, not knowing which LDS bytes they fill, wait for all of them before every transposing LDS
+// read, serialising the prefetch with the compute. Completion is waited for explicitly
+// (s_waitcnt vmcnt(0) before the barrier that publishes a tile). M0 is saved and restored because
+// the compiler owns it.
+__device__ __forceinline__ void lds_copy16(const char* base, uint32_t voff, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(voff), "s"(base)
+      : "memory");
 }
-template <int OFF>
-__device__ __forceinline__ void lds_read_tr16(s16x4& dst, uint32_t addr) {
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(dst) : "v"(addr), "i"(OFF));
+__device__ __forceinline__ void lds_copy16(const char* addr, uint32_t lds_addr) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds_addr), "v"(addr)
+      : "memory");
 }
-template <int N>
-__device__ __forceinline__ void lgkm_wait() {
-  static_assert(N >= 0 && N <= 15, "lgkmcnt range");
-  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N));
-}
-template <class T>
-__device__ __forceinline__ void after_wait(T& x) {
-  asm volatile("" : "+v"(x));  // orders uses of x after the preceding wait
-}
+__device__ __forceinline__ void vmem_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Map the flat workgroup id to (Q block, batch*head). Workgroups are handed to the 8 XCDs round
 // robin, so when B*H is a multiple of 8 each XCD gets its own set of heads (their K/V stay in that
@@ -162,18 +180,6 @@ __device__ __forceinline__ void map_block(int bid, int nq, int BH, int& qblk, in
     bh = bid - rank * BH;
   }
   qblk = CAUSAL ? (nq - 1 - rank) : rank;
-}
-
-// Number of LDS reads a step slot issues: one K read for a score slot, two V reads otherwise.
-template <int NS_QK>
-constexpr int slot_reads(int b) {
-  return b < NS_QK ? 1 : 2;
-}
-template <int NS_QK, int NS>
-constexpr int reads_between(int first, int last) {
-  int c = 0;
-  for (int x = first; x <= last && x < NS; ++x) c += slot_reads<NS_QK>(x);
-  return c;
 }
 
 template <class C>
@@ -210,20 +216,26 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   // LDS region (i*NW + w); it fetches the logical chunk that the swizzle puts there. Rows past T
   // are clamped to row T-1 (always in bounds); their scores are masked and their V rows zeroed.
   int dma_row[C::LOADS], dma_col[C::LOADS];
+  uint32_t dma_off[C::LOADS];
 #pragma unroll
   for (int i = 0; i < C::LOADS; ++i) {
     const int lofs = (i * NW + w) * 1024 + lane * 16;
     dma_row[i] = lofs / RB;
     dma_col[i] = swz<D>(dma_row[i], (lofs % RB) >> 4) * 16;
+    dma_off[i] = (uint32_t)(dma_row[i] * RB + dma_col[i]);
   }
   auto dma = [&](const char* g, int tile, int buf_off) {
     const int kt0 = tile * BN;
+    if (kt0 + BN <= T) {  // whole tile inside the sequence: scalar base + per-lane constant
+      const char* gt = g + (size_t)kt0 * RB;
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i) {
-      const uint32_t gofs = (uint32_t)(min(kt0 + dma_row[i], T - 1) * RB + dma_col[i]);
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(g + gofs),
-          (__attribute__((address_space(3))) void*)(smem + buf_off + (i * NW + w) * 1024), 16, 0, 0);
+      for (int i = 0; i < C::LOADS; ++i) lds_copy16(gt, dma_off[i], lds0 + buf_off + (i * NW + w) * 1024);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::LOADS; ++i) {
+        const uint32_t gofs = (uint32_t)(min(kt0 + dma_row[i], T - 1) * RB + dma_col[i]);
+        lds_copy16(g + gofs, lds0 + buf_off + (i * NW + w) * 1024);
+      }
     }
   };
   // Zero the V rows at or past T of a ragged last tile, so a clamped copy of row T-1 can never
@@ -255,13 +267,13 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   // ---- per-lane LDS byte addresses of the MFMA fragments (the buffer and the k-step / key block
   // parts are compile-time immediates).
   // K fragment (kb, s): row 32*kb + n, channels 16*s + 8*hf .. +7.
-  uint32_t k_addr[KSTEPS];
+  int k_off[KSTEPS];
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) k_addr[s] = lds0 + n * RB + swz<D>(n, 2 * s + hf) * 16;
+  for (int s = 0; s < KSTEPS; ++s) k_off[s] = n * RB + swz<D>(n, 2 * s + hf) * 16;
   // V^T fragment (t, cb): lane l (group g = l/16, i = l%16) holds V^T row c(cb, l%32) at the 8
   // keys of its P^T slots, via two transposing reads of 4 keys each. Source lane i of a group
   // reads V row (16*t + 4*(g/2) + i/4 [+ 8]) at 4 channels starting at the column below.
-  uint32_t v_addr[CB][2];
+  int v_off[CB][2];
   {
     const int grp = lane >> 4, gi = lane & 15;
     const int ga = grp & 1, gh = grp >> 1;
@@ -272,7 +284,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
         const int r = 4 * gh + e_src + 8 * rr;
-        v_addr[cb][rr] = lds0 + r * RB + swz<D>(r, col >> 3) * 16 + (col & 7) * 2;
+        v_off[cb][rr] = r * RB + swz<D>(r, col >> 3) * 16 + (col & 7) * 2;
       }
     }
   }
@@ -352,6 +364,13 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
       m_run[qb] = m_new;
     }
   };
+  auto read_k = [&](int buf_off, int kb, int s) {
+    return *reinterpret_cast<const bf16x8*>(smem + buf_off + kb * 32 * RB + k_off[s]);
+  };
+  auto read_v = [&](int buf_off, int t, int cb, int rr) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(smem + buf_off + t * 16 * RB + v_off[cb][rr]));
+  };
   auto pv_mfma = [&](int cb, int t, s16x4 lo, s16x4 hi) {
     const bf16x8 vfrag =
         __builtin_bit_cast(bf16x8, s16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
@@ -362,7 +381,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   };
 
   // ---- prologue: tiles 0 (K, V) and 1 (K) in LDS; S(0) = K(0) Q^T; first row max.
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  vmem_wait_all();
   __syncthreads();
   if (tail_ragged && n_tiles == 1) {
     zero_v_tail(C::VBUF0);
@@ -372,22 +391,15 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) sa[kb][qb] = f32x16{};
-  static_for<0, KSTEPS>([&](auto s_) {
-    constexpr int s = decltype(s_)::value;
-    bf16x8 kf[KB];
-    static_for<0, KB>([&](auto kb_) {
-      constexpr int kb = decltype(kb_)::value;
-      lds_read_b128<C::KBUF0 + kb * 32 * RB>(kf[kb], k_addr[s]);
-    });
-    lgkm_wait<0>();
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      after_wait(kf[kb]);
+      const bf16x8 kf = read_k(C::KBUF0, kb, s);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
-        sa[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[kb], qf[qb][s], sa[kb][qb], 0, 0, 0);
+        sa[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][s], sa[kb][qb], 0, 0, 0);
     }
-  });
   __syncthreads();  // every wave has read K(0) before K(2) is copied into its buffer
   if (needs_mask(0)) mask_tile(sa, 0);
 #pragma unroll
@@ -422,32 +434,27 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     auto issue = [&](auto b_) {
       constexpr int b = decltype(b_)::value;
       if constexpr (b < NS_QK) {
-        constexpr int s = b / KB, kb = b % KB;
-        lds_read_b128<KR + kb * 32 * RB>(kfr[b], k_addr[s]);
+        kfr[b] = read_k(KR, b % KB, b / KB);
       } else {
         constexpr int t = (b - NS_QK) / CB, cb = (b - NS_QK) % CB;
-        lds_read_tr16<VR + t * 16 * RB>(vfr[b - NS_QK][0], v_addr[cb][0]);
-        lds_read_tr16<VR + t * 16 * RB>(vfr[b - NS_QK][1], v_addr[cb][1]);
+        vfr[b - NS_QK][0] = read_v(VR, t, cb, 0);
+        vfr[b - NS_QK][1] = read_v(VR, t, cb, 1);
       }
     };
     static_for<0, PD>([&](auto b_) { issue(b_); });
 
     static_for<0, NS>([&](auto b_) {
       constexpr int b = decltype(b_)::value;
-      // prefetch slot b+PD, then wait until only the reads of slots b+1 .. b+PD are outstanding
+      // prefetch the fragments of slot b+PD (the compiler waits for slot b's before its MFMA)
       if constexpr (b + PD < NS) issue(std::integral_constant<int, b + PD>{});
-      lgkm_wait<reads_between<NS_QK, NS>(b + 1, b + PD)>();
       if constexpr (b < NS_QK) {
         constexpr int s = b / KB, kb = b % KB;
-        after_wait(kfr[b]);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           s_nxt[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
               kfr[b], qf[qb][s], s == 0 ? f32x16{} : s_nxt[kb][qb], 0, 0, 0);
       } else {
         constexpr int t = (b - NS_QK) / CB, cb = (b - NS_QK) % CB;
-        after_wait(vfr[b - NS_QK][0]);
-        after_wait(vfr[b - NS_QK][1]);
         pv_mfma(cb, t, vfr[b - NS_QK][0], vfr[b - NS_QK][1]);
       }
       // VALU work of this slot: the exp pairs assigned to it ...
@@ -461,16 +468,14 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
           for (int qb = 0; qb < QB; ++qb) exp_pair(s_cur, qb, p, neg_m[qb], lsum[qb]);
         });
       }
-      // ... the pending rescale of acc, spread over the score slots (before any P.V slot) ...
+      // ... the pending rescale of acc, spread over the score slots (before any P.V slot; a
+      // branch on "any row changed" would cost more in register copies than the multiplies) ...
       if constexpr (b < NS_QK) {
         constexpr int r0 = b * 16 / NS_QK, r1 = (b + 1) * 16 / NS_QK;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) rescale_chunk(qb, r0, r1);
       }
-      // ... and, once the next scores are complete, their mask and a chunk of their row max.
-      if constexpr (b == C::MAX_FIRST) {
-        if (mask_next) mask_tile(s_nxt, j + 1);
-      }
+      // ... and, once the next scores are complete, a chunk of their row max.
       if constexpr (b >= C::MAX_FIRST) {
         constexpr int nmax = NS - C::MAX_FIRST;
         constexpr int r0 = (b - C::MAX_FIRST) * 16 / nmax, r1 = (b - C::MAX_FIRST + 1) * 16 / nmax;
@@ -482,8 +487,16 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
 
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) l_run[qb] += lsum[qb];
+    if (mask_next) {  // diagonal or ragged tile: mask, then take the row max again
+      mask_tile(s_nxt, j + 1);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        mx[qb] = -__builtin_inff();
+        max_chunk(s_nxt, qb, 0, 16, mx[qb]);
+      }
+    }
     update_max(mx);
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    vmem_wait_all();
     __syncthreads();  // K(j+2), V(j+1) landed; every wave is done with K(j+1) and V(j)
     if (tail_ragged && j + 2 == n_tiles) {
       zero_v_tail(VW);
@@ -503,22 +516,10 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
       for (int p = 0; p < C::NPAIRS; ++p) exp_pair(s_cur, qb, p, neg_m, lsum);
       l_run[qb] = l_run[qb] * alpha[qb] + lsum;
     }
-    static_for<0, PT>([&](auto t_) {
-      constexpr int t = decltype(t_)::value;
-      s16x4 lo[CB], hi[CB];
-      static_for<0, CB>([&](auto cb_) {
-        constexpr int cb = decltype(cb_)::value;
-        lds_read_tr16<VR + t * 16 * RB>(lo[cb], v_addr[cb][0]);
-        lds_read_tr16<VR + t * 16 * RB>(hi[cb], v_addr[cb][1]);
-      });
-      lgkm_wait<0>();
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        after_wait(lo[cb]);
-        after_wait(hi[cb]);
-        pv_mfma(cb, t, lo[cb], hi[cb]);
-      }
-    });
+    for (int t = 0; t < PT; ++t)
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) pv_mfma(cb, t, read_v(VR, t, cb, 0), read_v(VR, t, cb, 1));
   };
 
   using K0 = std::integral_constant<int, C::KBUF0>;
