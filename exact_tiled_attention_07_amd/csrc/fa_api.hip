@@ -20,10 +20,10 @@ struct TileEntry {
   int lds_bytes;
 };
 
-template <int D, int QB, int NW, int BN>
+template <int D, int QB, int NW, int BN, int NSTAGE = 2>
 constexpr TileEntry entry() {
-  using Cc = fa::Cfg<D, QB, NW, BN, true>;
-  using Cf = fa::Cfg<D, QB, NW, BN, false>;
+  using Cc = fa::Cfg<D, QB, NW, BN, true, NSTAGE>;
+  using Cf = fa::Cfg<D, QB, NW, BN, false, NSTAGE>;
   return TileEntry{D, Cc::BM, BN, NW, &fa::fa_fwd_kernel<Cc>, &fa::fa_fwd_kernel<Cf>, Cc::LDS_BYTES};
 }
 

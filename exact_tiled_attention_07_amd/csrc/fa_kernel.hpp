@@ -29,9 +29,9 @@
 //   - The output is computed transposed too, O^T = V^T P^T: the P^T operand is exactly the S^T
 //     accumulator layout (after exp and bf16 rounding), and the rescale factor is per lane.
 //   - V^T comes from the row-major V tile through ds_read_b64_tr_b16 (a transposing LDS read).
-//   - K/V tiles go HBM -> LDS with global_load_lds_dwordx4 (no register staging); K is fetched two
-//     tiles ahead and V one tile ahead into separate double buffers, 16-byte chunks XOR-swizzled
-//     per row against LDS bank conflicts.
+//   - K/V tiles go HBM -> LDS with global_load_lds_dwordx4 (no register staging) into two rings of
+//     NSTAGE buffers; K is fetched NSTAGE tiles ahead and V NSTAGE-1 tiles ahead, so each copy has
+//     NSTAGE-1 steps to land. 16-byte chunks are XOR-swizzled per row against LDS bank conflicts.
 //   - Each wave is software-pipelined: in step j its MFMA "slots" first compute S(j+1) = K(j+1) Q^T
 //     and then O += V(j)^T P(j)^T, while the VALU work of the softmax of tile j (and the row max
 //     of S(j+1)) is spread over those slots. LDS fragments are read a few slots ahead.
@@ -55,19 +55,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-template <int D_, int QB_, int NW_, int BN_, bool CAUSAL_>
+template <int D_, int QB_, int NW_, int BN_, bool CAUSAL_, int NSTAGE_>
 struct Cfg {
   static constexpr int D = D_;        // head dim
   static constexpr int QB = QB_;      // 32-query column blocks per wave
   static constexpr int NW = NW_;      // waves per workgroup
   static constexpr int BN = BN_;      // keys per K/V tile
   static constexpr bool CAUSAL = CAUSAL_;
+  static constexpr int NSTAGE = NSTAGE_;            // LDS buffers per ring (K ring and V ring)
   static constexpr int BM = 32 * QB * NW;           // queries per workgroup
   static constexpr int THREADS = 64 * NW;
   static constexpr int ROW_BYTES = D * 2;           // one bf16 row of K or V
   static constexpr int CHUNKS = D / 8;              // 16-byte chunks per row
   static constexpr int TILE_BYTES = BN * ROW_BYTES; // one K (or V) tile
-  static constexpr int LDS_BYTES = 4 * TILE_BYTES;  // K0 K1 V0 V1
+  static constexpr int LDS_BYTES = 2 * NSTAGE * TILE_BYTES;  // K ring, then V ring
   static constexpr int LOADS = TILE_BYTES / (16 * THREADS);  // 16-byte loads per lane per tile
   static constexpr int KSTEPS = D / 16;             // k-steps of the score MFMA
   static constexpr int KB = BN / 32;                // 32-key blocks per tile
@@ -83,11 +84,12 @@ struct Cfg {
   static constexpr int EXP_WINDOW = NS_QK + (PT - 1) * CB;
   // the mask and row max of the next tile are spread over slots [MAX_FIRST, NS)
   static constexpr int MAX_FIRST = NS_QK + 2 < NS - 1 ? NS_QK + 2 : NS - 1;
-  static constexpr int KBUF0 = 0, KBUF1 = TILE_BYTES, VBUF0 = 2 * TILE_BYTES, VBUF1 = 3 * TILE_BYTES;
+  static constexpr int VRING = NSTAGE * TILE_BYTES; // offset of the V ring
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(BN % 32 == 0 && BN >= 32, "tile keys");
   static_assert(LOADS >= 1 && LOADS * 16 * THREADS == TILE_BYTES, "tile load split");
-  static_assert(LDS_BYTES <= 65536, "LDS immediate offsets are 16-bit");
+  static_assert(NSTAGE >= 2 && NSTAGE <= 4, "ring depth");
+  static_assert(LDS_BYTES <= 65536, "static LDS of one workgroup");
 };
 
 template <int I, int N, class F>
@@ -162,7 +164,11 @@ __device__ __forceinline__ void lds_copy16(const char* addr, uint32_t lds_addr) 
       : "s"(lds_addr), "v"(addr)
       : "memory");
 }
-__device__ __forceinline__ void vmem_wait_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+template <int N>
+__device__ __forceinline__ void vmem_wait() {  // all but the newest N vector-memory ops complete
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Map the flat workgroup id to (Q block, batch*head). Workgroups are handed to the 8 XCDs round
@@ -249,9 +255,12 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     }
   };
 
-  dma(kg, 0, C::KBUF0);
-  dma(vg, 0, C::VBUF0);
-  if (n_tiles > 1) dma(kg, 1, C::KBUF1);
+  // Prologue copies: K(0 .. NSTAGE-1) and V(0 .. NSTAGE-2) (clamped to the last tile).
+#pragma unroll
+  for (int t = 0; t < C::NSTAGE; ++t) {
+    if (t < n_tiles) dma(kg, t, t * C::TILE_BYTES);
+    if (t < C::NSTAGE - 1 && t < n_tiles) dma(vg, t, C::VRING + t * C::TILE_BYTES);
+  }
 
   // ---- Q fragments straight into registers: B operand of S^T = K Q^T. Lane (n, hf) holds
   // query row qw0 + 32*qb + n, channels 16*s + 8*hf .. +7.
@@ -381,10 +390,10 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   };
 
   // ---- prologue: tiles 0 (K, V) and 1 (K) in LDS; S(0) = K(0) Q^T; first row max.
-  vmem_wait_all();
+  vmem_wait<0>();
   __syncthreads();
-  if (tail_ragged && n_tiles == 1) {
-    zero_v_tail(C::VBUF0);
+  if (tail_ragged && n_tiles - 1 <= C::NSTAGE - 2) {  // the last V tile came with the prologue
+    zero_v_tail(C::VRING + (n_tiles - 1) * C::TILE_BYTES);
     __syncthreads();
   }
 #pragma unroll
@@ -395,7 +404,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const bf16x8 kf = read_k(C::KBUF0, kb, s);
+      const bf16x8 kf = read_k(0, kb, s);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         sa[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][s], sa[kb][qb], 0, 0, 0);
@@ -409,14 +418,14 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     m_run[qb] = wave_max_halves(mx) * scale_log2;  // key 0 is visible to every row: finite
   }
 
-  // ---- one pipelined step: softmax + P.V of tile j (scores in s_cur, V in buffer VR) while the
-  // scores of tile j+1 (K in buffer KR) go into s_nxt. Copies K(j+2) -> KW and V(j+1) -> VW.
-  auto step = [&](auto kr_, auto vr_, auto kw_, auto vw_, int j, f32x16 (&s_cur)[KB][QB],
+  // ---- one pipelined step: softmax + P.V of tile j (scores in s_cur, V at LDS offset VR) while
+  // the scores of tile j+1 (K at KR) go into s_nxt. Copies K(j+NSTAGE) -> KW and
+  // V(j+NSTAGE-1) -> VW (both buffers were consumed in the previous step).
+  auto step = [&](int j, int KR, int VR, int KW, int VW, f32x16 (&s_cur)[KB][QB],
                   f32x16 (&s_nxt)[KB][QB]) {
-    constexpr int KR = decltype(kr_)::value, VR = decltype(vr_)::value;
-    constexpr int KW = decltype(kw_)::value, VW = decltype(vw_)::value;
-    dma(kg, min(j + 2, n_tiles - 1), KW);  // past the end: a harmless re-copy of the last tile
-    dma(vg, j + 1, VW);
+    // past the end: harmless re-copies of the last tile into a buffer nobody reads any more
+    dma(kg, min(j + C::NSTAGE, n_tiles - 1), KW);
+    dma(vg, min(j + C::NSTAGE - 1, n_tiles - 1), VW);
 
     float neg_m[QB], lsum[QB], mx[QB];
 #pragma unroll
@@ -480,7 +489,11 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
         constexpr int nmax = NS - C::MAX_FIRST;
         constexpr int r0 = (b - C::MAX_FIRST) * 16 / nmax, r1 = (b - C::MAX_FIRST + 1) * 16 / nmax;
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) max_chunk(s_nxt, qb, r0, r1, mx[qb]);
+        for (int qb = 0; qb < QB; ++qb) {
+          max_chunk(s_nxt, qb, r0, r1, mx[qb]);
+          // keep the chunk in this slot (otherwise it sinks past the edge-tile branch below)
+          asm volatile("" : "+v"(mx[qb]));
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     });
@@ -496,17 +509,18 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
       }
     }
     update_max(mx);
-    vmem_wait_all();
-    __syncthreads();  // K(j+2), V(j+1) landed; every wave is done with K(j+1) and V(j)
-    if (tail_ragged && j + 2 == n_tiles) {
-      zero_v_tail(VW);
+    // the copies of the previous step (K(j+NSTAGE-1), V(j+NSTAGE-2)) have landed; this step's may
+    // still be in flight. The barrier publishes them and closes every wave's reads of K(j+1), V(j).
+    vmem_wait<2 * C::LOADS * (C::NSTAGE - 2)>();
+    __syncthreads();
+    if (tail_ragged && j + 2 == n_tiles && n_tiles - 1 > C::NSTAGE - 2) {  // V(n-1) just landed
+      zero_v_tail(C::VRING + ((n_tiles - 1) % C::NSTAGE) * C::TILE_BYTES);
       __syncthreads();
     }
   };
 
   // ---- last tile: softmax and P.V only.
-  auto last_step = [&](auto vr_, f32x16 (&s_cur)[KB][QB]) {
-    constexpr int VR = decltype(vr_)::value;
+  auto last_step = [&](int VR, f32x16 (&s_cur)[KB][QB]) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float lsum = 0.0f;
@@ -522,24 +536,32 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
       for (int cb = 0; cb < CB; ++cb) pv_mfma(cb, t, read_v(VR, t, cb, 0), read_v(VR, t, cb, 1));
   };
 
-  using K0 = std::integral_constant<int, C::KBUF0>;
-  using K1 = std::integral_constant<int, C::KBUF1>;
-  using V0 = std::integral_constant<int, C::VBUF0>;
-  using V1 = std::integral_constant<int, C::VBUF1>;
-  // Tile j's V sits in buffer j%2 and tile j+1's K in buffer (j+1)%2; unrolled by two so every
-  // buffer offset is an immediate and the score ping-pong needs no register copies.
+  // Tile t's K and V live in buffer t % NSTAGE of their rings. The loop is unrolled by two so the
+  // score ping-pong needs no register copies.
+  int ring_j = 0;  // j % NSTAGE
+  auto nxt = [](int r) { return r + 1 == C::NSTAGE ? 0 : r + 1; };
+  auto run_step = [&](int j, f32x16 (&s_cur)[KB][QB], f32x16 (&s_nxt)[KB][QB]) {
+    const int r1 = nxt(ring_j);                       // (j+1) % NSTAGE
+    const int rv = C::NSTAGE == 2 ? r1 : nxt(r1);     // (j+NSTAGE-1) % NSTAGE
+    step(j, r1 * C::TILE_BYTES, C::VRING + ring_j * C::TILE_BYTES, ring_j * C::TILE_BYTES,
+         C::VRING + rv * C::TILE_BYTES, s_cur, s_nxt);
+    ring_j = r1;
+  };
   for (int j = 0;; j += 2) {
     if (j + 1 >= n_tiles) {
-      last_step(V0{}, sa);
+      last_step(C::VRING + ring_j * C::TILE_BYTES, sa);
       break;
     }
-    step(K1{}, V0{}, K0{}, V1{}, j, sa, sb);
+    run_step(j, sa, sb);
     if (j + 2 >= n_tiles) {
-      last_step(V1{}, sb);
+      last_step(C::VRING + ring_j * C::TILE_BYTES, sb);
       break;
     }
-    step(K0{}, V1{}, K1{}, V0{}, j + 1, sb, sa);
+    run_step(j + 1, sb, sa);
   }
+  // Copies issued by the last steps may still be in flight (re-copies past the end); they must land
+  // before this workgroup's LDS can be handed to another one.
+  vmem_wait<0>();
 
   // ---- epilogue: O = acc / l, rounded once to bf16; LSE = ln2 * (m + log2 l).
   // Lane (n, hf) of channel block cb holds channels (D/2)*hf + 16*cb + r, r = 0..15, in order.
