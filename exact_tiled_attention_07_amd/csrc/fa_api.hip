@@ -30,6 +30,7 @@ constexpr TileEntry entry() {
 // Supported tile shapes. The first entry for each d is the default (see default_tile()).
 const TileEntry kTiles[] = {
     entry<64, 1, 4, 64>(),   // d=64: 128 queries (4 waves x 32), 64-key tiles
+    entry<64, 1, 4, 128>(),  // d=64: 128 queries (4 waves x 32), 128-key tiles
     entry<64, 1, 2, 64>(),   // d=64: 64 x 64, the tile shape of the tutorial page
     entry<64, 2, 2, 64>(),   // d=64: 128 queries (2 waves x 64)
     entry<64, 2, 4, 64>(),   // d=64: 256 queries (4 waves x 64)

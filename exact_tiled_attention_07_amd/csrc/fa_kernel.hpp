@@ -82,8 +82,11 @@ struct Cfg {
   // exp pairs are spread over slots [0, EXP_WINDOW); pair p must be done before the P.V slots of
   // its k-step p/4 start.
   static constexpr int EXP_WINDOW = NS_QK + (PT - 1) * CB;
-  // the mask and row max of the next tile are spread over slots [MAX_FIRST, NS)
-  static constexpr int MAX_FIRST = NS_QK + 2 < NS - 1 ? NS_QK + 2 : NS - 1;
+  // the row max of the next tile is spread over slots [MAX_FIRST, MAX_LAST]; slots NS-2 and NS-1
+  // combine the two wave halves and form the new max and alpha
+  static constexpr int MAX_FIRST = NS_QK + 2;
+  static constexpr int MAX_LAST = NS - 3;
+  static_assert(MAX_LAST >= MAX_FIRST, "slots for the row max");
   static constexpr int VRING = NSTAGE * TILE_BYTES; // offset of the V ring
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(BN % 32 == 0 && BN >= 32, "tile keys");
@@ -362,16 +365,11 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
 #pragma unroll
       for (int r = r0; r < r1; ++r) mx = fmaxf(mx, s[kb][qb][r]);
   };
-  // Online-softmax max update with the finished row max mx (raw scores) of the next tile; the
-  // factor for acc and l is applied while that tile is processed. A fully masked row chunk has
-  // mx = -inf and leaves m unchanged (alpha = 1).
-  auto update_max = [&](float (&mx)[QB]) {
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      const float m_new = fmaxf(m_run[qb], wave_max_halves(mx[qb]) * scale_log2);  // scale_log2 > 0
-      alpha[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-      m_run[qb] = m_new;
-    }
+  // Online-softmax max update from the row max mx (raw scores, this lane's half) of the next tile:
+  // the new max (scaled, base 2); the factor alpha = exp2(m_old - m_new) for acc and l is applied
+  // while that tile is processed. A fully masked row chunk has mx = -inf and leaves m unchanged.
+  auto new_max = [&](float mx, float m_old) {
+    return fmaxf(m_old, wave_max_halves(mx) * scale_log2);  // scale_log2 > 0 keeps the max
   };
   auto read_k = [&](int buf_off, int kb, int s) {
     return *reinterpret_cast<const bf16x8*>(smem + buf_off + kb * 32 * RB + k_off[s]);
@@ -427,7 +425,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     dma(kg, min(j + C::NSTAGE, n_tiles - 1), KW);
     dma(vg, min(j + C::NSTAGE - 1, n_tiles - 1), VW);
 
-    float neg_m[QB], lsum[QB], mx[QB];
+    float neg_m[QB], lsum[QB], mx[QB], m_spec[QB], a_spec[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       neg_m[qb] = -m_run[qb];
@@ -484,15 +482,30 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) rescale_chunk(qb, r0, r1);
       }
-      // ... and, once the next scores are complete, a chunk of their row max.
-      if constexpr (b >= C::MAX_FIRST) {
-        constexpr int nmax = NS - C::MAX_FIRST;
+      // ... and, once the next scores are complete, a chunk of their row max, then the new max and
+      // alpha (assuming the tile needs no mask; masked tiles redo this after the slots).
+      if constexpr (b >= C::MAX_FIRST && b <= C::MAX_LAST) {
+        constexpr int nmax = C::MAX_LAST - C::MAX_FIRST + 1;
         constexpr int r0 = (b - C::MAX_FIRST) * 16 / nmax, r1 = (b - C::MAX_FIRST + 1) * 16 / nmax;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           max_chunk(s_nxt, qb, r0, r1, mx[qb]);
           // keep the chunk in this slot (otherwise it sinks past the edge-tile branch below)
           asm volatile("" : "+v"(mx[qb]));
+        }
+      }
+      if constexpr (b == NS - 2) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          m_spec[qb] = new_max(mx[qb], m_run[qb]);
+          asm volatile("" : "+v"(m_spec[qb]));
+        }
+      }
+      if constexpr (b == NS - 1) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          a_spec[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_spec[qb]);
+          asm volatile("" : "+v"(a_spec[qb]));
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -504,11 +517,17 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
       mask_tile(s_nxt, j + 1);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        mx[qb] = -__builtin_inff();
-        max_chunk(s_nxt, qb, 0, 16, mx[qb]);
+        float m = -__builtin_inff();
+        max_chunk(s_nxt, qb, 0, 16, m);
+        m_spec[qb] = new_max(m, m_run[qb]);
+        a_spec[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_spec[qb]);
       }
     }
-    update_max(mx);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      m_run[qb] = m_spec[qb];
+      alpha[qb] = a_spec[qb];
+    }
     // the copies of the previous step (K(j+NSTAGE-1), V(j+NSTAGE-2)) have landed; this step's may
     // still be in flight. The barrier publishes them and closes every wave's reads of K(j+1), V(j).
     vmem_wait<2 * C::LOADS * (C::NSTAGE - 2)>();
