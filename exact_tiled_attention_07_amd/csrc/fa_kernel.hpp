@@ -556,7 +556,10 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   };
 
   // Tile t's K and V live in buffer t % NSTAGE of their rings. The loop is unrolled by two so the
-  // score ping-pong needs no register copies.
+  // score ping-pong needs no register copies, and it has a single exit with the last scores in sa:
+  // two exits (one per parity) would keep both register sets of the output accumulator and of the
+  // scores live through the whole loop. An odd number of steps runs its first step before the loop
+  // and moves its scores into sa once.
   int ring_j = 0;  // j % NSTAGE
   auto nxt = [](int r) { return r + 1 == C::NSTAGE ? 0 : r + 1; };
   auto run_step = [&](int j, f32x16 (&s_cur)[KB][QB], f32x16 (&s_nxt)[KB][QB]) {
@@ -566,18 +569,21 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
          C::VRING + rv * C::TILE_BYTES, s_cur, s_nxt);
     ring_j = r1;
   };
-  for (int j = 0;; j += 2) {
-    if (j + 1 >= n_tiles) {
-      last_step(C::VRING + ring_j * C::TILE_BYTES, sa);
-      break;
-    }
+  const int n_steps = n_tiles - 1;  // pipelined steps; the last tile is finished by last_step
+  int j0 = 0;
+  if (n_steps & 1) {
+    run_step(0, sa, sb);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sa[kb][qb] = sb[kb][qb];
+    j0 = 1;
+  }
+  for (int j = j0; j < n_steps; j += 2) {
     run_step(j, sa, sb);
-    if (j + 2 >= n_tiles) {
-      last_step(C::VRING + ring_j * C::TILE_BYTES, sb);
-      break;
-    }
     run_step(j + 1, sb, sa);
   }
+  last_step(C::VRING + ring_j * C::TILE_BYTES, sa);
   // Copies issued by the last steps may still be in flight (re-copies past the end); they must land
   // before this workgroup's LDS can be handed to another one.
   vmem_wait<0>();

@@ -156,7 +156,7 @@ def test_one_hot_values_expose_p():
 @pytest.mark.parametrize("d", [64, 128])
 def test_every_tile_shape(d):
     from exact_tiled_attention_07_amd.fa import lib  # noqa: F401  (library must be loaded)
-    shapes = {64: [(128, 64, 4), (64, 64, 2), (128, 64, 2), (256, 64, 4), (256, 64, 8)],
+    shapes = {64: [(128, 64, 4), (128, 128, 4), (64, 64, 2), (128, 64, 2), (256, 64, 4), (256, 64, 8)],
               128: [(128, 64, 4), (64, 64, 2)]}[d]
     qb, kb, vb = make_qkv(2, 3, 1000, d, seed=31 + d)
     scale = 1.0 / math.sqrt(d)
