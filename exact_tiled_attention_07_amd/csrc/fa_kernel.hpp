@@ -5,8 +5,9 @@
 //   - one workgroup owns one Q block of one (batch, head) and walks the K/V blocks; Q blocks never
 //     communicate (learn-llm.fim.ai "手写 FlashAttention：拆开 SDPA 这个黑盒", STEP 3);
 //   - per K/V block: scores on chip, running row max m and l = sum exp(x - m), and the output
-//     accumulator rescaled by alpha = exp(m_old - m_new) (same page, STEP 2); alpha is applied on
-//     every block (it is exactly 1 when the max did not grow), which keeps the loop branch-free;
+//     accumulator rescaled by alpha = exp(m_old - m_new) (same page, STEP 2); alpha is exactly 1
+//     when a row's max did not grow, and a wave skips the multiplications when that holds for all
+//     of its rows;
 //   - the division by l happens once, after the last block (same page, STEP 2, the note on
 //     FlashAttention-2 moving the divide to the end; cnblogs "内核案例研究：Flash Attention",
 //     section "块稀疏注意力 V2 和 V3", item 3);
@@ -122,10 +123,19 @@ __device__ __forceinline__ int swz(int r, int c) {
   }
 }
 
+// max of two floats as one v_max_f32. The row statistics never hold a signalling NaN, so the
+// quieting maxes the compiler puts in front of fmaxf for operands it cannot prove canonical (the
+// cross-lane swap below, values carried around the loop) are not needed.
+__device__ __forceinline__ float max_f32(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ __forceinline__ float wave_max_halves(float x) {
   // v_permlane32_swap(x, x) returns (x of lanes 0-31 twice, x of lanes 32-63 twice).
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_f32(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float wave_sum_halves(float x) {
@@ -240,9 +250,13 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) lds_copy16(gt, dma_off[i], lds0 + buf_off + (i * NW + w) * 1024);
     } else {
+      // the tile's first and the sequence's last row pass through an empty asm so that the
+      // per-lane clamping below stays in this (rare) branch instead of being hoisted into every step
+      int first = kt0, last = T - 1;
+      asm volatile("" : "+s"(first), "+s"(last));
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) {
-        const uint32_t gofs = (uint32_t)(min(kt0 + dma_row[i], T - 1) * RB + dma_col[i]);
+        const uint32_t gofs = (uint32_t)(min(first + dma_row[i], last) * RB + dma_col[i]);
         lds_copy16(g + gofs, lds0 + buf_off + (i * NW + w) * 1024);
       }
     }
@@ -258,11 +272,21 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     }
   };
 
+  // Tile t's K and V live in buffer (t + ring0) % NSTAGE of their rings. With two buffers per
+  // ring, ring0 is the parity of the number of pipelined steps, so that the steps taken in pairs
+  // (the main loop below) always start at buffer 0 and every LDS offset in the loop is an
+  // immediate; with more buffers ring0 is 0.
+  const int ring0 = C::NSTAGE == 2 ? ((n_tiles - 1) & 1) : 0;
+  auto buf_of = [&](int t) {
+    const int r = t % C::NSTAGE + ring0;
+    return r >= C::NSTAGE ? r - C::NSTAGE : r;
+  };
+
   // Prologue copies: K(0 .. NSTAGE-1) and V(0 .. NSTAGE-2) (clamped to the last tile).
 #pragma unroll
   for (int t = 0; t < C::NSTAGE; ++t) {
-    if (t < n_tiles) dma(kg, t, t * C::TILE_BYTES);
-    if (t < C::NSTAGE - 1 && t < n_tiles) dma(vg, t, C::VRING + t * C::TILE_BYTES);
+    if (t < n_tiles) dma(kg, t, buf_of(t) * C::TILE_BYTES);
+    if (t < C::NSTAGE - 1 && t < n_tiles) dma(vg, t, C::VRING + buf_of(t) * C::TILE_BYTES);
   }
 
   // ---- Q fragments straight into registers: B operand of S^T = K Q^T. Lane (n, hf) holds
@@ -344,7 +368,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     const int kb = p >> 3, r = (p & 7) * 2;
     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r], scale_log2, neg_m));
     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][qb][r + 1], scale_log2, neg_m));
-    lsum += p0 + p1;
+    lsum = p == 0 ? p0 + p1 : lsum + (p0 + p1);  // the first pair starts the sum
     uint32_t pk = pack_bf16x2(p0, p1);
     // keep this pair's work in the slot it was placed in (the optimizer would otherwise sink it
     // towards its P.V use, past the slots whose MFMAs it is meant to overlap)
@@ -369,7 +393,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   // the new max (scaled, base 2); the factor alpha = exp2(m_old - m_new) for acc and l is applied
   // while that tile is processed. A fully masked row chunk has mx = -inf and leaves m unchanged.
   auto new_max = [&](float mx, float m_old) {
-    return fmaxf(m_old, wave_max_halves(mx) * scale_log2);  // scale_log2 > 0 keeps the max
+    return max_f32(m_old, wave_max_halves(mx) * scale_log2);  // scale_log2 > 0 keeps the max
   };
   auto read_k = [&](int buf_off, int kb, int s) {
     return *reinterpret_cast<const bf16x8*>(smem + buf_off + kb * 32 * RB + k_off[s]);
@@ -391,7 +415,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   vmem_wait<0>();
   __syncthreads();
   if (tail_ragged && n_tiles - 1 <= C::NSTAGE - 2) {  // the last V tile came with the prologue
-    zero_v_tail(C::VRING + (n_tiles - 1) * C::TILE_BYTES);
+    zero_v_tail(C::VRING + buf_of(n_tiles - 1) * C::TILE_BYTES);
     __syncthreads();
   }
 #pragma unroll
@@ -402,7 +426,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const bf16x8 kf = read_k(0, kb, s);
+      const bf16x8 kf = read_k(buf_of(0) * C::TILE_BYTES, kb, s);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         sa[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][s], sa[kb][qb], 0, 0, 0);
@@ -434,6 +458,10 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
       mx[qb] = -__builtin_inff();
     }
     const bool mask_next = needs_mask(j + 1);
+    bool any_alpha = false;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) any_alpha |= alpha[qb] != 1.0f;
+    const bool need_rescale = __builtin_amdgcn_ballot_w64(any_alpha) != 0;
 
     // LDS fragment of slot b: one K read (score slots) or two transposing V reads (P.V slots).
     bf16x8 kfr[NS_QK];
@@ -475,12 +503,13 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
           for (int qb = 0; qb < QB; ++qb) exp_pair(s_cur, qb, p, neg_m[qb], lsum[qb]);
         });
       }
-      // ... the pending rescale of acc, spread over the score slots (before any P.V slot; a
-      // branch on "any row changed" would cost more in register copies than the multiplies) ...
-      if constexpr (b < NS_QK) {
-        constexpr int r0 = b * 16 / NS_QK, r1 = (b + 1) * 16 / NS_QK;
+      // ... the pending rescale of acc, in the first slot and skipped when no row of the wave has
+      // a new max (alpha is then exactly 1 in every lane: a wave-uniform branch) ...
+      if constexpr (b == 0) {
+        if (need_rescale) {
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) rescale_chunk(qb, r0, r1);
+          for (int qb = 0; qb < QB; ++qb) rescale_chunk(qb, 0, 16);
+        }
       }
       // ... and, once the next scores are complete, a chunk of their row max, then the new max and
       // alpha (assuming the tile needs no mask; masked tiles redo this after the slots).
@@ -533,7 +562,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     vmem_wait<2 * C::LOADS * (C::NSTAGE - 2)>();
     __syncthreads();
     if (tail_ragged && j + 2 == n_tiles && n_tiles - 1 > C::NSTAGE - 2) {  // V(n-1) just landed
-      zero_v_tail(C::VRING + ((n_tiles - 1) % C::NSTAGE) * C::TILE_BYTES);
+      zero_v_tail(C::VRING + buf_of(n_tiles - 1) * C::TILE_BYTES);
       __syncthreads();
     }
   };
@@ -555,12 +584,11 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
       for (int cb = 0; cb < CB; ++cb) pv_mfma(cb, t, read_v(VR, t, cb, 0), read_v(VR, t, cb, 1));
   };
 
-  // Tile t's K and V live in buffer t % NSTAGE of their rings. The loop is unrolled by two so the
-  // score ping-pong needs no register copies, and it has a single exit with the last scores in sa:
-  // two exits (one per parity) would keep both register sets of the output accumulator and of the
-  // scores live through the whole loop. An odd number of steps runs its first step before the loop
-  // and moves its scores into sa once.
-  int ring_j = 0;  // j % NSTAGE
+  // The loop is unrolled by two so the score ping-pong needs no register copies, and it has a
+  // single exit with the last scores in sa: two exits (one per parity) would keep both register
+  // sets of the output accumulator and of the scores live through the whole loop. An odd number
+  // of steps runs its first step before the loop and moves its scores into sa once.
+  int ring_j = ring0;  // buffer of tile j
   auto nxt = [](int r) { return r + 1 == C::NSTAGE ? 0 : r + 1; };
   auto run_step = [&](int j, f32x16 (&s_cur)[KB][QB], f32x16 (&s_nxt)[KB][QB]) {
     const int r1 = nxt(ring_j);                       // (j+1) % NSTAGE
@@ -579,6 +607,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
       for (int qb = 0; qb < QB; ++qb) sa[kb][qb] = sb[kb][qb];
     j0 = 1;
   }
+  if (C::NSTAGE == 2) ring_j = 0;  // tile j0 sits in buffer 0 (see ring0)
   for (int j = j0; j < n_steps; j += 2) {
     run_step(j, sa, sb);
     run_step(j + 1, sb, sa);
