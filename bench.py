@@ -5,7 +5,9 @@ Prints one JSON line:
   value        counted TFLOP/s of the step (2*B*H*T^2*d causal, 4*B*H*T^2*d non-causal)
   roofline     the kernel's achieved TFLOP/s from per-launch HIP events on its own stream,
                against the dense bf16 MFMA peak; traffic = HBM bytes per launch from rocprofv3
-               counters (when they were taken on the current kernel sources), else null
+               counters (when they were taken on the current kernel sources), else null; the same
+               holds for clock_mhz, the shader clock measured under the kernel, and the fraction
+               of the MFMA peak at that clock
   cpu_baseline the CPU oracle timed on the host cores on a bounded sample of the same workload
   sweep        the same measurement at the other sequence lengths of the metric (and d=128)
 
@@ -29,6 +31,8 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.
 KERNEL_SOURCES = ["exact_tiled_attention_07_amd/csrc/fa_kernel.hpp",
                   "exact_tiled_attention_07_amd/csrc/fa_api.hip"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_hbm_traffic.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_sq_counters.txt")
+MFMA_FLOP_PER_CLK = 256 * 4 * 1024  # dense bf16: 1024 flop per clock on each of the 1024 SIMDs
 
 
 def kernel_source_hash() -> str:
@@ -49,6 +53,19 @@ def recorded_traffic():
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
         return None
     return float(m_bytes.group(1))
+
+
+def recorded_clock_mhz():
+    """Shader clock measured under this kernel (GRBM_GUI_ACTIVE per XCD over the traced duration),
+    from the committed counter summary, if taken on these sources."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    text = open(COUNTERS_FILE).read()
+    m_hash = re.search(r"kernel_source_hash:\s*(\w+)", text)
+    m_clk = re.search(r"effective clock\s+([0-9.]+)\s*MHz", text)
+    if not m_hash or not m_clk or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_clk.group(1))
 
 
 def time_workload(wl, steps, warmup, tiles=None):
@@ -201,6 +218,8 @@ def main(argv=None):
         print(f"[bench] cpu baseline: {base}", file=sys.stderr, flush=True)
 
     traffic = recorded_traffic()
+    clock = recorded_clock_mhz()
+    peak_at_clock = MFMA_FLOP_PER_CLK * clock * 1e6 / 1e12 if clock else None
     line = {
         "metric": "causal attn fwd TFLOP/s & % of bf16 MFMA peak, B4 H12 d64, T=1K..16K",
         "value": round(value, 3),
@@ -221,6 +240,9 @@ def main(argv=None):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel_ms": round(kern_ms, 5),
+                     "clock_mhz": clock,
+                     "peak_at_clock": round(peak_at_clock, 1) if peak_at_clock else None,
+                     "frac_at_clock": round(achieved / peak_at_clock, 4) if peak_at_clock else None,
                      "flops_per_launch": wl.flops, **{k: round(v, 5) for k, v in extra.items()}},
         "cpu_baseline": base,
         "sweep": sweep,

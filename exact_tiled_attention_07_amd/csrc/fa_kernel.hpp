@@ -343,18 +343,22 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
 
   // ---- score-tile helpers -----------------------------------------------------------------
   // Mask tile `tile` of scores in place: key > query (causal) or key >= T become -inf.
+  // Register r of key block kb holds key kt0 + 4*hf + off with off = 32*kb + 8*(r/4) + r%4, a
+  // compile-time constant. The key is visible iff key <= last, last = min(query, T-1) (causal) or
+  // T-1, so each score needs one compare of the constant against a per-lane bound.
   auto mask_tile = [&](f32x16 (&s)[KB][QB], int tile) {
     const int kt0 = tile * BN;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int qi = qw0 + 32 * qb + n;
+      const int last = C::CAUSAL ? min(qi, T - 1) : T - 1;
+      const int bound = last - kt0 - 4 * hf;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kt0 + 32 * kb + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const bool visible = (key < T) && (!C::CAUSAL || key <= qi);
-          s[kb][qb][r] = visible ? s[kb][qb][r] : -__builtin_inff();
+          const int off = 32 * kb + 8 * (r >> 2) + (r & 3);
+          s[kb][qb][r] = off <= bound ? s[kb][qb][r] : -__builtin_inff();
         }
     }
   };

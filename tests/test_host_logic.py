@@ -25,6 +25,16 @@ def test_bench_traffic_record_matches_sources():
         assert t is None
 
 
+def test_bench_clock_record_matches_sources():
+    c = bench.recorded_clock_mhz()
+    text = open(bench.COUNTERS_FILE).read() if __import__("os").path.exists(bench.COUNTERS_FILE) else ""
+    if bench.kernel_source_hash() in text:
+        assert c is not None and 1000 < c < 2500
+    else:
+        assert c is None
+    assert bench.MFMA_FLOP_PER_CLK * 2.4e9 / 1e12 == pytest.approx(bench.PEAK_BF16_TFLOPS, rel=1e-4)
+
+
 def test_bench_cpu_baseline_small():
     r = bench.cpu_baseline(WORKLOADS["c1"], budget_s=1.0)
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["cores"] >= 1
