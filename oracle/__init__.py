@@ -1,4 +1,4 @@
-"""CPU oracle for exact attention forward — TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for exact attention, forward and backward — TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
 this package. The GPU library never imports, links or calls it, and this package imports nothing
@@ -15,8 +15,14 @@ naive, two-pass definition of attention on the bf16 inputs:
 * the natural-log logsumexp of each row's visible scaled scores is returned alongside ``O``
   (same page, STEP 4, the note on what the forward saves for the backward).
 
-Every function here is pinned by the ``not gpu`` tests in ``tests/test_oracle_pins.py``
-against closed forms, invariants and library special cases.
+``fa_ref_bwd.c`` holds the backward: the gradients of that forward with respect to ``Q``, ``K``
+and ``V`` for an output gradient ``dO``, with the probabilities recomputed from ``Q`` and ``K``
+(same page, STEP 4, the note on training; ijyty.com FlashAttention article, section 2.2), plus a
+float64-input forward with the same order of operations for finite-difference checks.
+
+Every function here is pinned by the ``not gpu`` tests in ``tests/test_oracle_pins.py`` and
+``tests/test_oracle_bwd_pins.py`` against closed forms, invariants, finite differences and library
+special cases.
 """
 from __future__ import annotations
 
@@ -28,6 +34,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fa_ref.c")
+_SRC_BWD = os.path.join(_HERE, "fa_ref_bwd.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
@@ -37,7 +44,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
-               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+               "-Wall", "-Wextra", "-o", tmp, _SRC, _SRC_BWD, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -62,6 +69,15 @@ def _load():
     lib.fa_ref_fwd_rows.restype = ctypes.c_int
     lib.fa_ref_threads_used.argtypes = [ctypes.c_int]
     lib.fa_ref_threads_used.restype = ctypes.c_int
+    lib.fa_ref_fwd_f64.argtypes = [p_f64, p_f64, p_f64, p_f64, p_f64, i64, i64, i64, i64,
+                                   ctypes.c_int, ctypes.c_double, ctypes.c_int]
+    lib.fa_ref_fwd_f64.restype = ctypes.c_int
+    lib.fa_ref_bwd_f64.argtypes = [p_f64, p_f64, p_f64, p_f64, p_f64, p_f64, p_f64, p_f64, i64, i64,
+                                   i64, i64, ctypes.c_int, ctypes.c_double, ctypes.c_int]
+    lib.fa_ref_bwd_f64.restype = ctypes.c_int
+    lib.fa_ref_bwd.argtypes = [p_u16, p_u16, p_u16, p_u16, p_f64, p_f64, p_f64, p_f64, i64, i64, i64,
+                               i64, ctypes.c_int, ctypes.c_double, ctypes.c_int]
+    lib.fa_ref_bwd.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -129,3 +145,76 @@ def attention_rows(q_bits, k_bits, v_bits, causal: bool, scale: float, rows, num
     if rc != 0:
         raise RuntimeError(f"fa_ref_fwd_rows failed with code {rc}")
     return o, lse
+
+
+def _as_f64(x, name: str) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    if a.ndim != 4:
+        raise ValueError(f"{name}: expected [B, H, T, d], got shape {a.shape}")
+    return a
+
+
+def attention_fwd_f64(q, k, v, causal: bool, scale: float, num_threads: int = 0):
+    """The forward on float64 inputs, in the same order of operations as ``attention_fwd``.
+
+    For checking the backward against finite differences of the forward. Returns ``(o, lse)``.
+    """
+    q, k, v = _as_f64(q, "q"), _as_f64(k, "k"), _as_f64(v, "v")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q/k/v shapes differ: {q.shape} {k.shape} {v.shape}")
+    B, H, T, d = q.shape
+    o = np.empty((B, H, T, d), dtype=np.float64)
+    lse = np.empty((B, H, T), dtype=np.float64)
+    rc = _load().fa_ref_fwd_f64(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
+                                _ptr(v, ctypes.c_double), _ptr(o, ctypes.c_double),
+                                _ptr(lse, ctypes.c_double), B, H, T, d, int(bool(causal)),
+                                float(scale), int(num_threads))
+    if rc != 0:
+        raise RuntimeError(f"fa_ref_fwd_f64 failed with code {rc}")
+    return o, lse
+
+
+def _bwd_out(shape):
+    B, H, T, d = shape
+    return (np.empty(shape, dtype=np.float64), np.empty(shape, dtype=np.float64),
+            np.empty(shape, dtype=np.float64), np.empty((B, H, T), dtype=np.float64))
+
+
+def attention_bwd(q_bits, k_bits, v_bits, do_bits, causal: bool, scale: float, num_threads: int = 0):
+    """Exact attention backward on bf16 inputs (uint16 bit patterns ``[B, H, T, d]``).
+
+    ``do_bits`` is the output gradient. The probabilities are recomputed from ``q`` and ``k`` in
+    float64 (nothing from a forward run is taken). Returns ``(dq, dk, dv, delta)``: float64
+    gradients ``[B, H, T, d]`` and ``delta[b, h, i] = dO_i . O_i`` ``[B, H, T]``.
+    """
+    q, k = _as_bf16_bits(q_bits, "q"), _as_bf16_bits(k_bits, "k")
+    v, do = _as_bf16_bits(v_bits, "v"), _as_bf16_bits(do_bits, "do")
+    if not (q.shape == k.shape == v.shape == do.shape):
+        raise ValueError(f"q/k/v/do shapes differ: {q.shape} {k.shape} {v.shape} {do.shape}")
+    B, H, T, d = q.shape
+    dq, dk, dv, delta = _bwd_out(q.shape)
+    rc = _load().fa_ref_bwd(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                            _ptr(v, ctypes.c_uint16), _ptr(do, ctypes.c_uint16),
+                            _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double),
+                            _ptr(dv, ctypes.c_double), _ptr(delta, ctypes.c_double),
+                            B, H, T, d, int(bool(causal)), float(scale), int(num_threads))
+    if rc != 0:
+        raise RuntimeError(f"fa_ref_bwd failed with code {rc}")
+    return dq, dk, dv, delta
+
+
+def attention_bwd_f64(q, k, v, do, causal: bool, scale: float, num_threads: int = 0):
+    """The backward on float64 inputs (for finite-difference and library checks)."""
+    q, k, v, do = _as_f64(q, "q"), _as_f64(k, "k"), _as_f64(v, "v"), _as_f64(do, "do")
+    if not (q.shape == k.shape == v.shape == do.shape):
+        raise ValueError(f"q/k/v/do shapes differ: {q.shape} {k.shape} {v.shape} {do.shape}")
+    B, H, T, d = q.shape
+    dq, dk, dv, delta = _bwd_out(q.shape)
+    rc = _load().fa_ref_bwd_f64(_ptr(q, ctypes.c_double), _ptr(k, ctypes.c_double),
+                                _ptr(v, ctypes.c_double), _ptr(do, ctypes.c_double),
+                                _ptr(dq, ctypes.c_double), _ptr(dk, ctypes.c_double),
+                                _ptr(dv, ctypes.c_double), _ptr(delta, ctypes.c_double),
+                                B, H, T, d, int(bool(causal)), float(scale), int(num_threads))
+    if rc != 0:
+        raise RuntimeError(f"fa_ref_bwd_f64 failed with code {rc}")
+    return dq, dk, dv, delta
