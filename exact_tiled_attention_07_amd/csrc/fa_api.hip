@@ -1,4 +1,4 @@
-// Host side of libfa.so: argument checks, the tile table, the launch plan and the kernel launch.
+// Host side of libfa.so: argument checks, the tile table, the launch plan and the kernel launches.
 // Declarations and the contract of every entry point are in include/fa.h.
 #include <hip/hip_runtime.h>
 
@@ -7,6 +7,7 @@
 #include <cstdint>
 
 #include "fa.h"
+#include "fa_bwd_kernel.hpp"
 #include "fa_kernel.hpp"
 
 namespace {
@@ -106,9 +107,62 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
   return FA_OK;
 }
 
+int launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+               const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int T,
+               int d, int causal, float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
+  int rc = check_sizes(B, H, T, d);
+  if (rc != FA_OK) return rc;
+  if (d != 64) return FA_ERR_UNSUPPORTED_D;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
+       (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u)
+    return FA_ERR_ALIGNMENT;
+  if (((uintptr_t)lse | (uintptr_t)delta) & 3u) return FA_ERR_ALIGNMENT;
+  const size_t n_elem = (size_t)B * H * T * d;
+  const size_t bytes = n_elem * 2, sbytes = (size_t)B * H * T * 4;
+  const void* ins[6] = {q, k, v, o, dout, lse};
+  const size_t in_bytes[6] = {bytes, bytes, bytes, bytes, bytes, sbytes};
+  const void* outs[4] = {dq, dk, dv, delta};
+  const size_t out_bytes[4] = {bytes, bytes, bytes, sbytes};
+  for (int a = 0; a < 4; ++a) {
+    for (int b = 0; b < 6; ++b)
+      if (overlaps(outs[a], out_bytes[a], ins[b], in_bytes[b])) return FA_ERR_INVALID_ARG;
+    for (int b = a + 1; b < 4; ++b)
+      if (overlaps(outs[a], out_bytes[a], outs[b], out_bytes[b])) return FA_ERR_INVALID_ARG;
+  }
+  if (n_elem == 0) return FA_OK;
+
+  using Cc = fa::BwdCfg<64, true>;
+  using Cf = fa::BwdCfg<64, false>;
+  const int nb = (T + Cc::BM - 1) / Cc::BM;  // query blocks (dQ kernel) = key blocks (dK/dV kernel)
+  const int BH = B * H;
+  const int64_t grid = (int64_t)nb * BH;
+  if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  const float scale_log2 = scale * fa::kLog2e;
+  hipStream_t s = (hipStream_t)stream;
+  auto dq_fn = causal ? &fa::fa_bwd_dq_kernel<Cc> : &fa::fa_bwd_dq_kernel<Cf>;
+  auto dkdv_fn = causal ? &fa::fa_bwd_dkdv_kernel<Cc> : &fa::fa_bwd_dkdv_kernel<Cf>;
+  hipLaunchKernelGGL(dq_fn, dim3((unsigned)grid), dim3(Cc::THREADS), 0, s, (const __bf16*)q,
+                     (const __bf16*)k, (const __bf16*)v, (const __bf16*)o, lse, (const __bf16*)dout,
+                     (__bf16*)dq, delta, T, nb, BH, scale, scale_log2);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  hipLaunchKernelGGL(dkdv_fn, dim3((unsigned)grid), dim3(Cc::THREADS), 0, s, (const __bf16*)q,
+                     (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dout,
+                     (const float*)delta, (__bf16*)dk, (__bf16*)dv, T, nb, BH, scale, scale_log2);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int T, int d,
+           int causal, float scale, void* stream) {
+  return launch_bwd(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, T, d, causal, scale, stream);
+}
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int T, int d,
            int causal, float scale, void* stream) {
@@ -152,8 +206,8 @@ const char* fa_strerror(int status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_INVALID_ARG: return "invalid argument (size out of range, scale not finite and > 0, or overlapping buffers)";
-    case FA_ERR_UNSUPPORTED_D: return "unsupported head dimension (d must be 64 or 128)";
-    case FA_ERR_ALIGNMENT: return "misaligned pointer (q, k, v, o need 16 bytes; lse needs 4)";
+    case FA_ERR_UNSUPPORTED_D: return "unsupported head dimension (d must be 64 or 128; 64 for fa_bwd)";
+    case FA_ERR_ALIGNMENT: return "misaligned pointer (bf16 tensors need 16 bytes; lse and delta need 4)";
     case FA_ERR_HIP: return "HIP runtime error at kernel launch";
     case FA_ERR_TILE: return "tile shape not in the supported table";
     default: return "unknown status";

@@ -1,9 +1,9 @@
 """ctypes binding of libfa.so (include/fa.h): argument marshalling only.
 
-Every step of the attention forward runs in the gfx950 HIP kernel behind ``fa_fwd``; this module
-checks tensor metadata, allocates outputs with torch when the caller gives none, and passes raw
-device pointers plus the current HIP stream. There is no fallback: if ``libfa.so`` is missing or
-a call fails, it raises.
+Every step of the attention forward runs in the gfx950 HIP kernel behind ``fa_fwd``, and every step
+of the backward in the two kernels behind ``fa_bwd``; this module checks tensor metadata, allocates
+outputs with torch when the caller gives none, and passes raw device pointers plus the current HIP
+stream. There is no fallback: if ``libfa.so`` is missing or a call fails, it raises.
 """
 from __future__ import annotations
 
@@ -55,6 +55,8 @@ def lib():
     L.fa_fwd_ex.restype = i
     L.fa_fwd_plan.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(PlanInfo)]
     L.fa_fwd_plan.restype = i
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    L.fa_bwd.restype = i
     L.fa_strerror.argtypes = [i]
     L.fa_strerror.restype = ctypes.c_char_p
     _lib = L
@@ -84,10 +86,10 @@ def plan(B: int, H: int, T: int, d: int, causal: bool = True, block_m: int = 0, 
     return {name: getattr(info, name) for name, _ in PlanInfo._fields_}
 
 
-def _check_inputs(q, k, v):
+def _check_inputs(q, k, v, *more):
     import torch
 
-    for name, t in (("q", q), ("k", k), ("v", v)):
+    for name, t in (("q", q), ("k", k), ("v", v), *more):
         if not isinstance(t, torch.Tensor):
             raise TypeError(f"{name} must be a torch.Tensor")
         if t.dtype != torch.bfloat16:
@@ -102,6 +104,9 @@ def _check_inputs(q, k, v):
         raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on the same device")
+    for name, t in more:
+        if t.shape != q.shape or t.device != q.device:
+            raise ValueError(f"{name} must be shaped like q and on q's device")
 
 
 def _outputs(q, out, lse):
@@ -161,3 +166,41 @@ def fwd_ex(q, k, v, block_m: int, block_n: int, waves: int, causal: bool = True,
                                lse.data_ptr(), B, H, T, d, int(bool(causal)), scale,
                                _stream_handle(q.device, stream), block_m, block_n, waves))
     return out, lse
+
+
+def _like(q, t, name, dtype=None, shape=None):
+    import torch
+
+    dtype = q.dtype if dtype is None else dtype
+    shape = tuple(q.shape) if shape is None else shape
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=q.device)
+    if t.dtype != dtype or tuple(t.shape) != shape or not t.is_contiguous() or t.device != q.device:
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor {shape} on q's device")
+    return t
+
+
+def bwd(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None, dq=None, dk=None,
+        dv=None, delta=None, stream=None):
+    """Exact attention backward on the GPU (``fa_bwd``): returns ``(dq, dk, dv, delta)``.
+
+    ``o`` and ``lse`` are the outputs of ``fwd`` for the same q, k, v, causal and scale; ``dout`` is
+    the gradient of the loss with respect to ``o``. All bfloat16 tensors are contiguous
+    ``[B, H, T, 64]`` on the GPU; lse is float32 ``[B, H, T]``. Returns bfloat16 gradients shaped
+    like q and ``delta`` float32 ``[B, H, T]`` (``dO_i . O_i``).
+    """
+    import torch
+
+    _check_inputs(q, k, v, ("o", o), ("dout", dout))
+    B, H, T, d = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, T]")
+    dq, dk, dv = _like(q, dq, "dq"), _like(q, dk, "dk"), _like(q, dv, "dv")
+    delta = _like(q, delta, "delta", torch.float32, (B, H, T))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        _check(lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                            dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                            delta.data_ptr(), B, H, T, d, int(bool(causal)), scale,
+                            _stream_handle(q.device, stream)))
+    return dq, dk, dv, delta

@@ -1,7 +1,7 @@
 /*
- * fa.h — C-ABI of the MI355X (gfx950) exact tiled attention forward library (libfa.so).
+ * fa.h — C-ABI of the MI355X (gfx950) exact tiled attention library (libfa.so).
  *
- * The one operation is the fused, tiled, exact attention forward
+ * The main operation is the fused, tiled, exact attention forward
  *
  *     O[b,h,i,:] = sum_j P[i,j] V[b,h,j,:],   P[i,:] = softmax_j( scale * Q[b,h,i,:] . K[b,h,j,:] )
  *     LSE[b,h,i] = ln sum_j exp( scale * Q[b,h,i,:] . K[b,h,j,:] )
@@ -17,6 +17,7 @@
  *     same page, STEP 4;
  *   - the Q-block-parallel ordering that keeps m and l on chip: cnblogs
  *     "内核案例研究：Flash Attention", section "块稀疏注意力 V2 和 V3".
+ * Its gradients (fa_bwd) are computed from the saved logsumexp by recomputation.
  *
  * Conventions shared by every entry point:
  *   - Tensors are row-major and contiguous. q, k, v and o are bf16 [B, H, T, d] (the innermost
@@ -99,6 +100,34 @@ typedef struct fa_plan_info {
  */
 int fa_fwd_plan(int B, int H, int T, int d, int causal, int block_m, int block_n, int waves,
                 fa_plan_info* out);
+
+/*
+ * fa_bwd — exact attention backward (gradients of fa_fwd), by recomputation from the saved LSE.
+ *
+ *     dV = P^T dO,  dP = dO V^T,  D_i = dO_i . O_i,  dS = P o (dP - D),
+ *     dQ = scale dS K,  dK = scale dS^T Q,   with P = exp(scale Q K^T - LSE) over the visible keys
+ *
+ * The forward keeps only O and the per-row logsumexp; the backward recomputes the scores and the
+ * probabilities block by block instead of storing the T x T matrix (learn-llm.fim.ai
+ * "手写 FlashAttention：拆开 SDPA 这个黑盒", STEP 4, the note on training; ijyty.com
+ * FlashAttention article, section 2.2: recomputation, and gradients accumulated per block).
+ *   q, k, v  [in]  bf16 [B, H, T, d], device, 16-byte aligned: the forward's inputs
+ *   o        [in]  bf16 [B, H, T, d], device, 16-byte aligned: the forward's output
+ *   lse      [in]  fp32 [B, H, T], device, 4-byte aligned: the forward's logsumexp
+ *   dout     [in]  bf16 [B, H, T, d], device, 16-byte aligned: the gradient of the loss wrt o
+ *   dq, dk, dv [out] bf16 [B, H, T, d], device, 16-byte aligned; rounded to nearest even
+ *   delta    [out] fp32 [B, H, T], device, 4-byte aligned: D_i = dO_i . O_i (written, then read by
+ *                  the second kernel; its content after the call is that value)
+ *   B, H, T, causal, scale, stream: as for fa_fwd (o and lse must come from fa_fwd with the same
+ *   q, k, causal and scale)
+ *   d        head dimension: 64 (d = 128 returns FA_ERR_UNSUPPORTED_D)
+ * The outputs dq, dk, dv and delta must not overlap each other or any input. Two kernels run in
+ * order on `stream` (dQ and D, then dK and dV); no atomics, no allocation.
+ * Returns FA_OK or a negative fa_status (checked before anything is launched).
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int T, int d,
+           int causal, float scale, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* fa_strerror(int status);

@@ -21,7 +21,7 @@ def call(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=1, T=8, d=64, causal=
 
 def test_library_exports_every_declared_function():
     names = fa.header_functions()
-    assert names == ["fa_fwd", "fa_fwd_ex", "fa_fwd_plan", "fa_strerror"]
+    assert names == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_fwd_plan", "fa_strerror"]
     lib = fa.lib()
     for n in names:
         assert hasattr(lib, n)
@@ -128,3 +128,51 @@ def test_plan_errors():
         fa.plan(1, 1, 8, 64, True, 96, 64, 3)
     assert e.value.status == fa.FA_ERR_TILE
     assert fa.lib().fa_fwd_plan(1, 1, 8, 64, 1, 0, 0, 0, None) == fa.FA_ERR_NULL
+
+
+# ---- fa_bwd: the same checks, before anything is launched
+BW = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, dout=6 * A, dq=7 * A, dk=8 * A, dv=9 * A,
+          delta=10 * A)
+
+
+def call_bwd(B=1, H=1, T=8, d=64, causal=1, scale=0.125, **kw):
+    p = dict(BW, **kw)
+    return fa.lib().fa_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["dout"], p["dq"], p["dk"],
+                           p["dv"], p["delta"], B, H, T, d, causal, scale, None)
+
+
+def test_bwd_null_pointers():
+    for name in BW:
+        assert call_bwd(**{name: None}) == fa.FA_ERR_NULL, name
+
+
+def test_bwd_sizes_head_dim_scale():
+    assert call_bwd(T=-1) == fa.FA_ERR_INVALID_ARG
+    assert call_bwd(B=1 << 13, H=1 << 12) == fa.FA_ERR_INVALID_ARG
+    assert call_bwd(d=128) == fa.FA_ERR_UNSUPPORTED_D  # the backward is d = 64 only
+    assert call_bwd(d=32) == fa.FA_ERR_UNSUPPORTED_D
+    for sc in (0.0, -1.0, float("nan"), float("inf")):
+        assert call_bwd(scale=sc) == fa.FA_ERR_INVALID_ARG
+
+
+def test_bwd_alignment():
+    for name in ("q", "k", "v", "o", "dout", "dq", "dk", "dv"):
+        assert call_bwd(**{name: BW[name] + 8}) == fa.FA_ERR_ALIGNMENT, name
+    for name in ("lse", "delta"):
+        assert call_bwd(**{name: BW[name] + 2}) == fa.FA_ERR_ALIGNMENT, name
+        assert call_bwd(T=0, **{name: BW[name] + 4}) == fa.FA_OK, name
+
+
+def test_bwd_overlaps():
+    # each bf16 tensor is 1 KiB at T=8, d=64; lse/delta 32 B
+    assert call_bwd(dq=A + 512) == fa.FA_ERR_INVALID_ARG       # output over an input
+    assert call_bwd(dk=7 * A + 256) == fa.FA_ERR_INVALID_ARG   # output over another output
+    assert call_bwd(delta=5 * A + 16) == fa.FA_ERR_INVALID_ARG  # over lse
+    assert call_bwd(delta=9 * A + 1020) == fa.FA_ERR_INVALID_ARG  # over dv
+
+
+@pytest.mark.parametrize("shape", [(0, 3, 8, 64), (2, 0, 8, 64), (2, 3, 0, 64)])
+def test_bwd_empty_problem_is_ok(shape):
+    B, H, T, d = shape
+    assert call_bwd(B=B, H=H, T=T, d=d) == fa.FA_OK
+    assert call_bwd(B=B, H=H, T=T, d=d, causal=0) == fa.FA_OK

@@ -1,0 +1,153 @@
+"""Parity of the gfx950 backward (fa_bwd, through the C-ABI) with the CPU fp64 backward oracle.
+
+The GPU backward takes the GPU forward's O and LSE (as a training step would); the oracle recomputes
+everything from the bf16 Q, K, V and dO in fp64. Tolerance (derived from the arithmetic, see
+``grad_tolerance``): the algorithm must use the forward's bf16 O in D = dO . O, round P and dS to
+bf16 before the matrix products, and round the gradients to bf16 at the end. A CPU model of exactly
+those roundings, on the inputs of this file, reaches an element error of 0.108 (|ref| + rms of the
+head) in dQ for the sigma-4 scores (the dominant weight's dS is a small difference of two large
+terms, and the rounding of O enters through D) and an RMS error of 0.59% of the RMS. The bounds
+below are about twice that: 0.2 (|ref| + rms) per element and 1.5% RMS.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exact_tiled_attention_07_amd as fa
+from exact_tiled_attention_07_amd.inputs import WORKLOADS, bf16_bits_from_f32, bf16_bits_to_f32, make_qkv, to_torch_bf16
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+ELEM_TOL = 0.2    # |gpu - ref| <= ELEM_TOL * (|ref| + rms of the reference over its head)
+RMS_TOL = 0.015   # rms(gpu - ref) <= RMS_TOL * rms(ref), per tensor
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def grad_tolerance(name, gpu, ref):
+    """Element and RMS check of one gradient tensor [B, H, T, d] (or delta [B, H, T])."""
+    axes = tuple(range(2, ref.ndim))
+    rms_head = np.sqrt((ref ** 2).mean(axis=axes, keepdims=True))
+    err = np.abs(gpu - ref)
+    ratio = err / (np.abs(ref) + rms_head + 1e-30)
+    rms_ratio = math.sqrt(float((err ** 2).mean()) / max(float((ref ** 2).mean()), 1e-300))
+    stats = {"max_err": float(err.max()) if err.size else 0.0,
+             "max_ratio": float(ratio.max()) if err.size else 0.0, "rms_ratio": rms_ratio,
+             "nonfinite": int((~np.isfinite(gpu)).sum())}
+    assert stats["nonfinite"] == 0, (name, stats)
+    assert stats["max_ratio"] <= ELEM_TOL, (name, stats)
+    assert rms_ratio <= RMS_TOL, (name, stats)
+    return stats
+
+
+def run_gpu(qb, kb, vb, dob, causal, scale):
+    q, k, v, do = (to_torch_bf16(x, DEV) for x in (qb, kb, vb, dob))
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv, delta = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv, delta)]
+
+
+def check(qb, kb, vb, dob, causal, scale, label):
+    say(f"[gpu bwd] {label} shape={qb.shape} causal={causal} scale={scale}")
+    got = run_gpu(qb, kb, vb, dob, causal, scale)
+    ref = oracle.attention_bwd(qb, kb, vb, dob, causal, scale)
+    stats = {n: grad_tolerance(n, g, r) for n, g, r in zip(("dq", "dk", "dv", "delta"), got, ref)}
+    say(f"[gpu bwd] {label} " + " ".join(f"{n}: {s['max_ratio']:.4f}/{s['rms_ratio']:.4f}"
+                                         for n, s in stats.items()))
+    return got, ref
+
+
+def inputs(B, H, T, seed, sigma=1.0):
+    qb, kb, vb = make_qkv(B, H, T, 64, seed=seed, sigma=sigma)
+    dob, _, _ = make_qkv(B, H, T, 64, seed=seed + 7919)
+    return qb, kb, vb, dob
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("T", [1, 2, 31, 63, 64, 65, 127, 128, 129, 255, 257, 1000])
+def test_bwd_ragged_and_tiny_lengths(T, causal):
+    check(*inputs(1, 3, T, 2000 + T), causal, 0.125, f"T={T}")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_bwd_configs(name):
+    wl = WORKLOADS[name]
+    qb, kb, vb = wl.make()
+    dob, _, _ = make_qkv(wl.B, wl.H, wl.T, wl.d, seed=wl.seed + 7919)
+    check(qb, kb, vb, dob, wl.causal, wl.scale, wl.name)
+
+
+def test_bwd_long_sequence():
+    # one twelfth of the T = 4096 workload (4 of its 48 heads), inputs at its sigma of 2
+    check(*inputs(1, 4, 4096, 4, sigma=2.0), True, 0.125, "T=4096 sigma2 (4 heads)")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_bwd_other_scales_and_wide_scores(causal):
+    check(*inputs(2, 2, 300, 77), causal, 0.01, "scale=0.01")
+    check(*inputs(2, 2, 300, 78), causal, 1.0, "scale=1.0")
+    qb, kb, _, dob = inputs(1, 4, 700, 5, sigma=4.0)
+    _, _, vb, _ = inputs(1, 4, 700, 6)
+    check(qb, kb, vb, dob, causal, 0.125, "sigma4 q/k")
+
+
+def test_bwd_closed_forms():
+    T = 200
+    _, kb, vb, dob = inputs(1, 2, T, 21)
+    # Q = 0: every dK is an exact zero (dK = scale dS^T Q)
+    qz = np.zeros_like(kb)
+    got, ref = check(qz, kb, vb, dob, True, 0.125, "Q=0")
+    np.testing.assert_array_equal(got[1], 0.0)
+    # sum over keys of dV equals the sum over queries of dO (rows of P sum to one)
+    qb, kb, vb, dob = inputs(1, 2, T, 22)
+    got, _ = check(qb, kb, vb, dob, False, 0.125, "sum dV")
+    do = bf16_bits_to_f32(dob).astype(np.float64)
+    np.testing.assert_allclose(got[2].sum(axis=2), do.sum(axis=2), rtol=0.02, atol=0.05)
+    # all V rows equal: O does not depend on the scores, so dQ and dK vanish up to rounding
+    row = np.random.default_rng(3).standard_normal(64).astype(np.float32)
+    vconst = bf16_bits_from_f32(np.broadcast_to(row, (1, 2, T, 64)).copy())
+    got = run_gpu(qb, kb, vconst, dob, True, 0.125)
+    assert np.abs(got[0]).max() < 0.02 and np.abs(got[1]).max() < 0.02, (np.abs(got[0]).max(), np.abs(got[1]).max())
+
+
+def test_bwd_writes_stay_inside_outputs_and_are_deterministic():
+    B, H, T, d = 2, 3, 333, 64
+    qb, kb, vb, dob = inputs(B, H, T, 41)
+    q, k, v, do = (to_torch_bf16(x, DEV) for x in (qb, kb, vb, dob))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    n, nl, guard = B * H * T * d, B * H * T, 4096
+    bigs = [torch.full((n + 2 * guard,), float("nan"), dtype=torch.bfloat16, device=DEV) for _ in range(3)]
+    dbig = torch.full((nl + 2 * guard,), float("nan"), dtype=torch.float32, device=DEV)
+    dq, dk, dv = (b[guard:guard + n].view(B, H, T, d) for b in bigs)
+    delta = dbig[guard:guard + nl].view(B, H, T)
+    fa.bwd(q, k, v, o, lse, do, causal=True, dq=dq, dk=dk, dv=dv, delta=delta)
+    torch.cuda.synchronize()
+    for b in bigs:
+        assert torch.isnan(b[:guard].float()).all() and torch.isnan(b[guard + n:].float()).all()
+    assert torch.isnan(dbig[:guard]).all() and torch.isnan(dbig[guard + nl:]).all()
+    for t in (dq, dk, dv, delta):
+        assert torch.isfinite(t.float()).all()
+    again = fa.bwd(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    for a, b in zip((dq, dk, dv), again[:3]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert torch.equal(delta, again[3])
+
+
+def test_bwd_binding_rejects():
+    q = torch.zeros(1, 1, 8, 128, dtype=torch.bfloat16, device=DEV)
+    lse = torch.zeros(1, 1, 8, dtype=torch.float32, device=DEV)
+    with pytest.raises(fa.FaError):  # the backward supports d = 64 only
+        fa.bwd(q, q, q, q, lse, q)
+    q64 = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        fa.bwd(q64, q64, q64, q64, lse[..., :4], q64)
+    with pytest.raises(TypeError):
+        fa.bwd(q64, q64, q64, q64.float(), lse, q64)
