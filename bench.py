@@ -10,8 +10,11 @@ Prints one JSON line:
                of the MFMA peak at that clock
   cpu_baseline the CPU oracle timed on the host cores on a bounded sample of the same workload
   sweep        the same measurement at the other sequence lengths of the metric (and d=128)
+  backward     fa_bwd (dQ, dK, dV from the forward's O and LSE) on the same workload: counted
+               TFLOP/s with the usual 2.5x-forward count, per-launch HIP events around both kernels
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4] [--no-cpu-baseline]
+                       [--no-sweep] [--no-backward] [--only-backward]
 """
 from __future__ import annotations
 
@@ -30,6 +33,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 KERNEL_SOURCES = ["exact_tiled_attention_07_amd/csrc/fa_kernel.hpp",
                   "exact_tiled_attention_07_amd/csrc/fa_api.hip"]
+BWD_FLOPS_PER_FWD = 2.5  # the usual count: the backward's matrix products are 2.5x the forward's
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_hbm_traffic.txt")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_sq_counters.txt")
 MFMA_FLOP_PER_CLK = 256 * 4 * 1024  # dense bf16: 1024 flop per clock on each of the 1024 SIMDs
@@ -123,6 +127,47 @@ def time_workload(wl, steps, warmup, tiles=None):
                              "cold_ms": cold_ms}
 
 
+def time_backward(wl, steps, warmup):
+    """fa_bwd on the workload's inputs (o and lse from one fa_fwd, dO drawn like the inputs).
+
+    Returns (avg ms per fa_bwd call from per-launch events on the launch stream, extra stats)."""
+    import torch
+
+    import exact_tiled_attention_07_amd as fa
+    from exact_tiled_attention_07_amd.inputs import make_qkv, to_torch_bf16
+
+    dev = torch.device("cuda:0")
+    q, k, v = (to_torch_bf16(x, dev) for x in wl.make())
+    do = to_torch_bf16(make_qkv(wl.B, wl.H, wl.T, wl.d, seed=wl.seed + 7919)[0], dev)
+    o, lse = fa.fwd(q, k, v, causal=wl.causal, scale=wl.scale)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    delta = torch.empty_like(lse)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        fa.bwd(q, k, v, o, lse, do, causal=wl.causal, scale=wl.scale, dq=dq, dk=dk, dv=dv,
+               delta=delta, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize(dev)
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize(dev)
+    durs = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+    return sum(durs) / len(durs), {"wall_ms": wall_ms, "median_ms": durs[len(durs) // 2],
+                                    "min_ms": durs[0], "max_ms": durs[-1]}
+
+
 def cpu_baseline(wl, budget_s=20.0):
     """Time the CPU oracle on a bounded sample of the workload (whole heads, all host cores)."""
     import numpy as np
@@ -164,6 +209,9 @@ def main(argv=None):
     ap.add_argument("--tiles", default=None, help="force BMxBNxWAVES (fa_fwd_ex)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--only-backward", action="store_true",
+                    help="time fa_bwd only and print its line (for profiling the backward)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this size (for counter calibration)")
     args = ap.parse_args(argv)
@@ -184,6 +232,18 @@ def main(argv=None):
         return 1
     tiles = tuple(int(x) for x in args.tiles.split("x")) if args.tiles else None
     wl = WORKLOADS[args.workload]
+    backward = None
+    if not args.no_backward and wl.d == 64:
+        bms, bex = time_backward(wl, args.steps, args.warmup)
+        bfl = BWD_FLOPS_PER_FWD * wl.flops
+        backward = {"workload": wl.name, "ms_per_step": round(bms, 5),
+                    "tflops": round(bfl / (bms * 1e-3) / 1e12, 3),
+                    "pct_of_peak": round(100 * bfl / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                    "flops_counted": bfl, **{k2: round(v2, 5) for k2, v2 in bex.items()}}
+        print(f"[bench] backward {wl.name}: {backward}", file=sys.stderr, flush=True)
+        if args.only_backward:
+            print(json.dumps({"backward": backward}), flush=True)
+            return 0
     wall_ms, kern_ms, extra = time_workload(wl, args.steps, args.warmup, tiles)
     value = wl.flops / (wall_ms * 1e-3) / 1e12
     achieved = wl.flops / (kern_ms * 1e-3) / 1e12
@@ -246,6 +306,7 @@ def main(argv=None):
                      "flops_per_launch": wl.flops, **{k: round(v, 5) for k, v in extra.items()}},
         "cpu_baseline": base,
         "sweep": sweep,
+        "backward": backward,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -341,8 +341,8 @@ __global__ __launch_bounds__(C::THREADS) void fa_bwd_dkdv_kernel(
 #pragma unroll
     for (int qb = 0; qb < KB; ++qb) {
       const int qs = qt0 + 32 * qb;  // first query of this 32-row block
-      // every query of the block precedes every key of this wave: nothing is visible
-      if (C::CAUSAL && qs + 31 < kw0) continue;
+      // (a block whose queries all precede this wave's keys is computed and masked whole: a branch
+      // around it raised the kernel from 196 to 252 VGPRs and measured 8-12% slower overall)
       // S = Q K^T and dP = dO V^T: rows = queries 8*(r/4) + 4*hf + r%4 of the block, column = key
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
