@@ -34,27 +34,30 @@ PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.
 KERNEL_SOURCES = ["exact_tiled_attention_07_amd/csrc/fa_kernel.hpp",
                   "exact_tiled_attention_07_amd/csrc/fa_api.hip"]
 BWD_FLOPS_PER_FWD = 2.5  # the usual count: the backward's matrix products are 2.5x the forward's
+BWD_SOURCES = ["exact_tiled_attention_07_amd/csrc/fa_bwd_kernel.hpp"] + KERNEL_SOURCES
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_bwd_c4_hbm_traffic.txt")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_hbm_traffic.txt")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_sq_counters.txt")
 MFMA_FLOP_PER_CLK = 256 * 4 * 1024  # dense bf16: 1024 flop per clock on each of the 1024 SIMDs
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes per launch from the committed counter summary, if taken on these sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+def recorded_traffic(path=None, sources=None):
+    """HBM bytes per launch from a committed counter summary, if taken on these sources."""
+    path = TRAFFIC_FILE if path is None else path
+    if not os.path.exists(path):
         return None
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     m_hash = re.search(r"kernel_source_hash:\s*(\w+)", text)
     m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(sources):
         return None
     return float(m_bytes.group(1))
 
@@ -200,6 +203,20 @@ def cpu_baseline(wl, budget_s=20.0):
                       f"fp64 two-pass oracle, {dt:.1f} s"}
 
 
+def copy_calibration(mib):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    if not mib:
+        return
+    import torch
+
+    src = torch.ones(mib << 20, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f"[bench] copy calibration: 3 copies of {mib} MiB", file=sys.stderr)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -236,12 +253,17 @@ def main(argv=None):
     if not args.no_backward and wl.d == 64:
         bms, bex = time_backward(wl, args.steps, args.warmup)
         bfl = BWD_FLOPS_PER_FWD * wl.flops
-        backward = {"workload": wl.name, "ms_per_step": round(bms, 5),
-                    "tflops": round(bfl / (bms * 1e-3) / 1e12, 3),
-                    "pct_of_peak": round(100 * bfl / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-                    "flops_counted": bfl, **{k2: round(v2, 5) for k2, v2 in bex.items()}}
+        bach = bfl / (bms * 1e-3) / 1e12
+        backward = {"workload": wl.name, "ms_per_step": round(bms, 5), "tflops": round(bach, 3),
+                    "pct_of_peak": round(100 * bach / PEAK_BF16_TFLOPS, 2), "flops_counted": bfl,
+                    **{k2: round(v2, 5) for k2, v2 in bex.items()},
+                    "roofline": {"bound": "mfma", "achieved": round(bach, 3), "peak": PEAK_BF16_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(bach / PEAK_BF16_TFLOPS, 4),
+                                 "traffic": recorded_traffic(BWD_TRAFFIC_FILE, BWD_SOURCES)},
+                    "kernel_source_hash": kernel_source_hash(BWD_SOURCES)}
         print(f"[bench] backward {wl.name}: {backward}", file=sys.stderr, flush=True)
         if args.only_backward:
+            copy_calibration(args.copy_calibration_mib)
             print(json.dumps({"backward": backward}), flush=True)
             return 0
     wall_ms, kern_ms, extra = time_workload(wl, args.steps, args.warmup, tiles)
@@ -263,14 +285,7 @@ def main(argv=None):
                            "pct_of_peak": round(100 * w2.flops / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
             print(f"[bench] sweep {w2.name}: {sweep[name]}", file=sys.stderr, flush=True)
 
-    if args.copy_calibration_mib:
-        n = args.copy_calibration_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(f"[bench] copy calibration: 3 copies of {args.copy_calibration_mib} MiB", file=sys.stderr)
+    copy_calibration(args.copy_calibration_mib)
 
     base = None
     if not args.no_cpu_baseline:

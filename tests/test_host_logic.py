@@ -25,6 +25,16 @@ def test_bench_traffic_record_matches_sources():
         assert t is None
 
 
+def test_bench_backward_traffic_record_matches_sources():
+    t = bench.recorded_traffic(bench.BWD_TRAFFIC_FILE, bench.BWD_SOURCES)
+    os_ = __import__("os")
+    text = open(bench.BWD_TRAFFIC_FILE).read() if os_.path.exists(bench.BWD_TRAFFIC_FILE) else ""
+    if bench.kernel_source_hash(bench.BWD_SOURCES) in text:
+        assert t is not None and t > 0
+    else:
+        assert t is None
+
+
 def test_bench_clock_record_matches_sources():
     c = bench.recorded_clock_mhz()
     text = open(bench.COUNTERS_FILE).read() if __import__("os").path.exists(bench.COUNTERS_FILE) else ""
