@@ -20,8 +20,13 @@ and ``V`` for an output gradient ``dO``, with the probabilities recomputed from 
 (same page, STEP 4, the note on training; ijyty.com FlashAttention article, section 2.2), plus a
 float64-input forward with the same order of operations for finite-difference checks.
 
+``fa_ref_sparse.c`` holds the block-sparse forward: keys of a (query block, key block) whose mask
+is zero are not visible, the way the causal mask hides the blocks above the diagonal (cnblogs
+"内核案例研究：Flash Attention", section "块稀疏注意力 V2 和 V3"); a row with no visible key gets
+``O = 0`` and ``LSE = -inf``.
+
 Every function here is pinned by the ``not gpu`` tests in ``tests/test_oracle_pins.py`` and
-``tests/test_oracle_bwd_pins.py`` against closed forms, invariants, finite differences and library
+``tests/test_oracle_bwd_pins.py`` and ``tests/test_oracle_sparse_pins.py`` against closed forms, invariants, finite differences and library
 special cases.
 """
 from __future__ import annotations
@@ -35,6 +40,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fa_ref.c")
 _SRC_BWD = os.path.join(_HERE, "fa_ref_bwd.c")
+_SRC_SPARSE = os.path.join(_HERE, "fa_ref_sparse.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
@@ -44,7 +50,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-fno-fast-math",
-               "-Wall", "-Wextra", "-o", tmp, _SRC, _SRC_BWD, "-lm"]
+               "-Wall", "-Wextra", "-o", tmp, _SRC, _SRC_BWD, _SRC_SPARSE, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -78,6 +84,10 @@ def _load():
     lib.fa_ref_bwd.argtypes = [p_u16, p_u16, p_u16, p_u16, p_f64, p_f64, p_f64, p_f64, i64, i64, i64,
                                i64, ctypes.c_int, ctypes.c_double, ctypes.c_int]
     lib.fa_ref_bwd.restype = ctypes.c_int
+    lib.fa_ref_fwd_blockmask.argtypes = [p_u16, p_u16, p_u16, p_f64, p_f64, i64, i64, i64, i64,
+                                         ctypes.c_int, ctypes.c_double,
+                                         ctypes.POINTER(ctypes.c_uint8), i64, i64, i64, ctypes.c_int]
+    lib.fa_ref_fwd_blockmask.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -218,3 +228,31 @@ def attention_bwd_f64(q, k, v, do, causal: bool, scale: float, num_threads: int 
     if rc != 0:
         raise RuntimeError(f"fa_ref_bwd_f64 failed with code {rc}")
     return dq, dk, dv, delta
+
+
+def attention_fwd_blockmask(q_bits, k_bits, v_bits, causal: bool, scale: float, mask,
+                            block_m: int, block_n: int, num_threads: int = 0):
+    """Block-sparse attention forward on bf16 inputs.
+
+    ``mask`` is uint8 ``[mask_heads, ceil(T/block_m), ceil(T/block_n)]`` with ``mask_heads`` 1 or
+    ``B*H``; key j is visible to query i iff the mask of (i // block_m, j // block_n) is nonzero
+    (and j <= i when causal). Rows with no visible key get ``O = 0``, ``LSE = -inf``.
+    """
+    q, k, v = _as_bf16_bits(q_bits, "q"), _as_bf16_bits(k_bits, "k"), _as_bf16_bits(v_bits, "v")
+    if not (q.shape == k.shape == v.shape):
+        raise ValueError(f"q/k/v shapes differ: {q.shape} {k.shape} {v.shape}")
+    B, H, T, d = q.shape
+    m = np.ascontiguousarray(np.asarray(mask, dtype=np.uint8))
+    nqb, nkb = -(-T // block_m), -(-T // block_n)
+    if m.ndim != 3 or m.shape[1:] != (nqb, nkb) or m.shape[0] not in (1, B * H):
+        raise ValueError(f"mask must be [1 or B*H, {nqb}, {nkb}], got {m.shape}")
+    o = np.empty((B, H, T, d), dtype=np.float64)
+    lse = np.empty((B, H, T), dtype=np.float64)
+    rc = _load().fa_ref_fwd_blockmask(_ptr(q, ctypes.c_uint16), _ptr(k, ctypes.c_uint16),
+                                      _ptr(v, ctypes.c_uint16), _ptr(o, ctypes.c_double),
+                                      _ptr(lse, ctypes.c_double), B, H, T, d, int(bool(causal)),
+                                      float(scale), _ptr(m, ctypes.c_uint8), m.shape[0], block_m,
+                                      block_n, int(num_threads))
+    if rc != 0:
+        raise RuntimeError(f"fa_ref_fwd_blockmask failed with code {rc}")
+    return o, lse
