@@ -12,6 +12,9 @@ Prints one JSON line:
   sweep        the same measurement at the other sequence lengths of the metric (and d=128)
   backward     fa_bwd (dQ, dK, dV from the forward's O and LSE) on the same workload: counted
                TFLOP/s with the usual 2.5x-forward count, per-launch HIP events around both kernels
+  sparse       fa_fwd_sparse at T=16384 (B4 H12 d64 causal) under a seeded block mask (25% of the
+               128x64 blocks plus the diagonal ones): TFLOP/s over the visible (query, key) pairs
+               and the time against the dense forward of the same shape
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4] [--no-cpu-baseline]
                        [--no-sweep] [--no-backward] [--only-backward]
@@ -171,6 +174,77 @@ def time_backward(wl, steps, warmup):
                                     "min_ms": durs[0], "max_ms": durs[-1]}
 
 
+def sparse_mask(T, density, seed):
+    """The bench's block mask: each 128x64 block kept with probability `density`, plus the blocks
+    on the diagonal (so every query sees a key)."""
+    import numpy as np
+
+    nq, nk = -(-T // 128), -(-T // 64)
+    m = (np.random.Generator(np.random.PCG64(seed)).random((1, nq, nk)) < density).astype(np.uint8)
+    for i in range(nq):
+        m[0, i, 2 * i:min(nk, 2 * i + 2)] = 1
+    return m
+
+
+def visible_pairs(mask, T, causal):
+    """Number of (query, key) pairs a block mask leaves visible (per head)."""
+    import numpy as np
+
+    nq, nk = mask.shape[1:]
+    rows = np.arange(T)
+    total = 0
+    for qb in range(nq):
+        r = rows[qb * 128:min(T, qb * 128 + 128)]
+        for kb in np.nonzero(mask[0, qb])[0]:
+            j0, j1 = kb * 64, min(T, kb * 64 + 64)
+            if causal:
+                total += int(np.clip(np.minimum(r + 1, j1) - j0, 0, None).sum())
+            else:
+                total += r.size * (j1 - j0)
+    return total
+
+
+def time_sparse(wl, steps, warmup, density=0.25):
+    """fa_fwd_sparse vs fa_fwd on the same inputs; returns the bench line's `sparse` object."""
+    import torch
+
+    import exact_tiled_attention_07_amd as fa
+    from exact_tiled_attention_07_amd.inputs import to_torch_bf16
+
+    dev = torch.device("cuda:0")
+    q, k, v = (to_torch_bf16(x, dev) for x in wl.make())
+    mask_np = sparse_mask(wl.T, density, wl.seed)
+    mask = torch.from_numpy(mask_np).to(dev)
+    o, lse = torch.empty_like(q), torch.empty((wl.B, wl.H, wl.T), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize(dev)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for i in range(steps):
+            starts[i].record(stream)
+            fn()
+            ends[i].record(stream)
+        torch.cuda.synchronize(dev)
+        return sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / steps
+
+    ms_sparse = timed(lambda: fa.fwd_sparse(q, k, v, mask, causal=wl.causal, scale=wl.scale, out=o,
+                                            lse=lse, stream=stream))
+    ms_dense = timed(lambda: fa.fwd(q, k, v, causal=wl.causal, scale=wl.scale, out=o, lse=lse,
+                                    stream=stream))
+    pairs = visible_pairs(mask_np, wl.T, wl.causal)
+    flops = 4.0 * wl.d * pairs * wl.B * wl.H
+    dense_pairs = wl.T * (wl.T + 1) // 2 if wl.causal else wl.T * wl.T
+    return {"workload": wl.name, "mask": f"{density:.0%} random 128x64 blocks + diagonal, seed {wl.seed}",
+            "visible_fraction": round(pairs / dense_pairs, 4), "ms_per_step": round(ms_sparse, 5),
+            "tflops": round(flops / (ms_sparse * 1e-3) / 1e12, 3),
+            "pct_of_peak": round(100 * flops / (ms_sparse * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+            "dense_ms": round(ms_dense, 5), "speedup_vs_dense": round(ms_dense / ms_sparse, 3)}
+
+
 def cpu_baseline(wl, budget_s=20.0):
     """Time the CPU oracle on a bounded sample of the workload (whole heads, all host cores)."""
     import numpy as np
@@ -227,6 +301,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-sparse", action="store_true")
     ap.add_argument("--only-backward", action="store_true",
                     help="time fa_bwd only and print its line (for profiling the backward)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -285,6 +360,11 @@ def main(argv=None):
                            "pct_of_peak": round(100 * w2.flops / (kms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2)}
             print(f"[bench] sweep {w2.name}: {sweep[name]}", file=sys.stderr, flush=True)
 
+    sparse = None
+    if not args.no_sparse:
+        sparse = time_sparse(WORKLOADS["c5a"], max(5, args.steps // 10), max(2, args.warmup // 10))
+        print(f"[bench] sparse: {sparse}", file=sys.stderr, flush=True)
+
     copy_calibration(args.copy_calibration_mib)
 
     base = None
@@ -322,6 +402,7 @@ def main(argv=None):
         "cpu_baseline": base,
         "sweep": sweep,
         "backward": backward,
+        "sparse": sparse,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

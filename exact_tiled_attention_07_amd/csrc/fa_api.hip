@@ -13,7 +13,7 @@
 namespace {
 
 using KernelFn = void (*)(const __bf16*, const __bf16*, const __bf16*, __bf16*, float*, int, int, int,
-                          float);
+                          float, const uint8_t*, int);
 
 struct TileEntry {
   int d, block_m, block_n, waves;
@@ -102,7 +102,53 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
   KernelFn fn = causal ? tile->causal_fn : tile->full_fn;
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * tile->waves), 0, (hipStream_t)stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, T, nq, BH,
-                     scale_log2);
+                     scale_log2, (const uint8_t*)nullptr, 0);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+// Block-sparse forward: the default tile shape (128 queries x 64 keys per tile, 4 waves) with the
+// tile list built from the caller's mask.
+template <int D>
+struct SparseFns {
+  using Cc = fa::Cfg<D, 1, 4, 64, true, 2, true>;
+  using Cf = fa::Cfg<D, 1, 4, 64, false, 2, true>;
+  static_assert(Cc::BM == FA_SPARSE_BLOCK_M && Cc::BN == FA_SPARSE_BLOCK_N, "mask blocks = tiles");
+  static_assert(Cc::MAX_LIST * Cc::BN >= FA_SPARSE_MAX_T, "tile list capacity");
+};
+
+int launch_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int T, int d, int causal, float scale, const unsigned char* block_mask,
+                  int mask_heads, void* stream) {
+  if (!q || !k || !v || !o || !lse || !block_mask) return FA_ERR_NULL;
+  int rc = check_sizes(B, H, T, d);
+  if (rc != FA_OK) return rc;
+  if (T > FA_SPARSE_MAX_T) return FA_ERR_INVALID_ARG;
+  if (mask_heads != 1 && (int64_t)mask_heads != (int64_t)B * H) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGNMENT;
+  if ((uintptr_t)lse & 3u) return FA_ERR_ALIGNMENT;
+  const size_t n_elem = (size_t)B * H * T * d;
+  const size_t bytes = n_elem * 2, lse_bytes = (size_t)B * H * T * 4;
+  const int nq = (T + FA_SPARSE_BLOCK_M - 1) / FA_SPARSE_BLOCK_M;
+  const int nk = (T + FA_SPARSE_BLOCK_N - 1) / FA_SPARSE_BLOCK_N;
+  const size_t mask_bytes = (size_t)mask_heads * nq * nk;
+  const void* ins[4] = {q, k, v, block_mask};
+  const size_t in_bytes[4] = {bytes, bytes, bytes, mask_bytes};
+  for (int a = 0; a < 4; ++a)
+    if (overlaps(o, bytes, ins[a], in_bytes[a]) || overlaps(lse, lse_bytes, ins[a], in_bytes[a]))
+      return FA_ERR_INVALID_ARG;
+  if (overlaps(o, bytes, lse, lse_bytes)) return FA_ERR_INVALID_ARG;
+  if (n_elem == 0) return FA_OK;
+  const int BH = B * H;
+  const int64_t grid = (int64_t)nq * BH;
+  if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  KernelFn fn;
+  if (d == 64) fn = causal ? &fa::fa_fwd_kernel<SparseFns<64>::Cc> : &fa::fa_fwd_kernel<SparseFns<64>::Cf>;
+  else fn = causal ? &fa::fa_fwd_kernel<SparseFns<128>::Cc> : &fa::fa_fwd_kernel<SparseFns<128>::Cf>;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, (const __bf16*)q,
+                     (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, T, nq, BH,
+                     scale * fa::kLog2e, (const uint8_t*)block_mask, mask_heads);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }
@@ -157,6 +203,12 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* o, const
 }  // namespace
 
 extern "C" {
+
+int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int T, int d, int causal, float scale, const unsigned char* block_mask,
+                  int mask_heads, void* stream) {
+  return launch_sparse(q, k, v, o, lse, B, H, T, d, causal, scale, block_mask, mask_heads, stream);
+}
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int T, int d,

@@ -55,8 +55,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kSparseMaxFloor = -1.0e30f;  // running-max floor of the block-sparse path
 
-template <int D_, int QB_, int NW_, int BN_, bool CAUSAL_, int NSTAGE_>
+template <int D_, int QB_, int NW_, int BN_, bool CAUSAL_, int NSTAGE_, bool SPARSE_ = false>
 struct Cfg {
   static constexpr int D = D_;        // head dim
   static constexpr int QB = QB_;      // 32-query column blocks per wave
@@ -64,6 +65,10 @@ struct Cfg {
   static constexpr int BN = BN_;      // keys per K/V tile
   static constexpr bool CAUSAL = CAUSAL_;
   static constexpr int NSTAGE = NSTAGE_;            // LDS buffers per ring (K ring and V ring)
+  // block-sparse: a per-(Q block, K/V tile) mask selects the tiles a workgroup visits; their
+  // indices are compacted into an LDS list (at most MAX_LIST tiles, i.e. T <= MAX_LIST * BN)
+  static constexpr bool SPARSE = SPARSE_;
+  static constexpr int MAX_LIST = SPARSE_ ? 1024 : 0;
   static constexpr int BM = 32 * QB * NW;           // queries per workgroup
   static constexpr int THREADS = 64 * NW;
   static constexpr int ROW_BYTES = D * 2;           // one bf16 row of K or V
@@ -204,7 +209,8 @@ __device__ __forceinline__ void map_block(int bid, int nq, int BH, int& qblk, in
 template <class C>
 __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    __bf16* __restrict__ o, float* __restrict__ lse, int T, int nq, int BH, float scale_log2) {
+    __bf16* __restrict__ o, float* __restrict__ lse, int T, int nq, int BH, float scale_log2,
+    const uint8_t* __restrict__ bmask, int mask_heads) {
   constexpr int D = C::D, QB = C::QB, NW = C::NW, BN = C::BN, BM = C::BM;
   constexpr int KB = C::KB, CB = C::CB, PT = C::PT, KSTEPS = C::KSTEPS, RB = C::ROW_BYTES;
   constexpr int NS_QK = C::NS_QK, NS = C::NS, PD = C::PD;
@@ -216,6 +222,8 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform per wave
   const int n = lane & 31;    // query column of this lane within a 32-query block
   const int hf = lane >> 5;   // which half of the wave (0/1)
+  (void)bmask;
+  (void)mask_heads;
 
   int qblk, bh;
   map_block<C::CAUSAL>(blockIdx.x, nq, BH, qblk, bh);
@@ -228,8 +236,57 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   // K/V tiles this workgroup needs: up to the diagonal when causal (tiles above it are never
   // touched), all of them otherwise. The last one reaches past T only for a ragged end.
   const int kv_end = C::CAUSAL ? min(q0 + BM, T) : T;
-  const int n_tiles = (kv_end + BN - 1) / BN;
-  const bool tail_ragged = n_tiles * BN > T;
+  const int n_cand = (kv_end + BN - 1) / BN;  // candidate tiles 0 .. n_cand-1
+  // Block-sparse: keep the candidates whose mask byte is nonzero, in ascending order, as a list in
+  // LDS; tile_at(x) is the x-th tile visited (the identity when dense).
+  __shared__ uint16_t tlist[C::SPARSE ? C::MAX_LIST : 1];
+  __shared__ int wcount[C::SPARSE ? NW : 1];
+  int n_tiles = n_cand;
+  if constexpr (C::SPARSE) {
+    const uint8_t* mrow = bmask + ((int64_t)(mask_heads == 1 ? 0 : bh) * nq + qblk) * ((T + BN - 1) / BN);
+    int count = 0;
+    for (int base = 0; base < n_cand; base += C::THREADS) {
+      const int t = base + tid;
+      const bool on = t < n_cand && mrow[t] != 0;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
+      if (lane == 0) wcount[w] = __builtin_popcountll(bal);
+      __syncthreads();
+      int before = 0, total = 0;
+#pragma unroll
+      for (int x = 0; x < NW; ++x) {
+        const int c = wcount[x];
+        before += x < w ? c : 0;
+        total += c;
+      }
+      const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      if (on) tlist[count + before + below] = (uint16_t)t;
+      count += total;
+      __syncthreads();
+    }
+    n_tiles = __builtin_amdgcn_readfirstlane(count);
+  }
+  auto tile_at = [&](int x) -> int {
+    if constexpr (C::SPARSE) return __builtin_amdgcn_readfirstlane((int)tlist[x]);
+    else return x;
+  };
+  if constexpr (C::SPARSE) {
+    if (n_tiles == 0) {  // no key visible to any row of the block: O = 0, LSE = -inf
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int row = qw0 + 32 * qb + n;
+        if (row < T) {
+          u32x4* orow = reinterpret_cast<u32x4*>(o + head_off + (int64_t)row * D);
+#pragma unroll
+          for (int c = 0; c < D / 16; ++c) orow[2 * c + hf] = u32x4{0u, 0u, 0u, 0u};
+          if (hf == 0) lse[(int64_t)bh * T + row] = -__builtin_inff();
+        }
+      }
+      return;
+    }
+  }
+  const int last_tile = tile_at(n_tiles - 1);
+  const bool tail_ragged = (last_tile + 1) * BN > T;
 
   // ---- HBM -> LDS copies of one K or V tile. Lane `lane` of load i fills 16 bytes of the 1 KiB
   // LDS region (i*NW + w); it fetches the logical chunk that the swizzle puts there. Rows past T
@@ -264,7 +321,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   // Zero the V rows at or past T of a ragged last tile, so a clamped copy of row T-1 can never
   // reach the output (their weights are 0; a non-finite input row would still give 0 * inf).
   auto zero_v_tail = [&](int buf_off) {
-    const int first = T - (n_tiles - 1) * BN;  // first row to clear, 0 < first < BN
+    const int first = T - last_tile * BN;  // first row to clear, 0 < first < BN
     char* vl = smem + buf_off;
     for (int idx = tid; idx < (BN - first) * C::CHUNKS; idx += C::THREADS) {
       const int r = first + idx / C::CHUNKS;
@@ -285,8 +342,8 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   // Prologue copies: K(0 .. NSTAGE-1) and V(0 .. NSTAGE-2) (clamped to the last tile).
 #pragma unroll
   for (int t = 0; t < C::NSTAGE; ++t) {
-    if (t < n_tiles) dma(kg, t, buf_of(t) * C::TILE_BYTES);
-    if (t < C::NSTAGE - 1 && t < n_tiles) dma(vg, t, C::VRING + buf_of(t) * C::TILE_BYTES);
+    if (t < n_tiles) dma(kg, tile_at(t), buf_of(t) * C::TILE_BYTES);
+    if (t < C::NSTAGE - 1 && t < n_tiles) dma(vg, tile_at(t), C::VRING + buf_of(t) * C::TILE_BYTES);
   }
 
   // ---- Q fragments straight into registers: B operand of S^T = K Q^T. Lane (n, hf) holds
@@ -436,12 +493,16 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
         sa[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][s], sa[kb][qb], 0, 0, 0);
     }
   __syncthreads();  // every wave has read K(0) before K(2) is copied into its buffer
-  if (needs_mask(0)) mask_tile(sa, 0);
+  if (needs_mask(tile_at(0))) mask_tile(sa, tile_at(0));
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     float mx = -__builtin_inff();
     max_chunk(sa, qb, 0, 16, mx);
-    m_run[qb] = wave_max_halves(mx) * scale_log2;  // key 0 is visible to every row: finite
+    m_run[qb] = wave_max_halves(mx) * scale_log2;  // dense: key 0 is visible to every row: finite
+    // block-sparse: a row may see no key of its first tile (or of any); a finite floor keeps
+    // exp2(s - m) at 0 for masked scores instead of NaN, and the floor is left behind (with
+    // alpha = 0) as soon as the row sees a key
+    if constexpr (C::SPARSE) m_run[qb] = max_f32(m_run[qb], kSparseMaxFloor);
   }
 
   // ---- one pipelined step: softmax + P.V of tile j (scores in s_cur, V at LDS offset VR) while
@@ -450,8 +511,8 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   auto step = [&](int j, int KR, int VR, int KW, int VW, f32x16 (&s_cur)[KB][QB],
                   f32x16 (&s_nxt)[KB][QB]) {
     // past the end: harmless re-copies of the last tile into a buffer nobody reads any more
-    dma(kg, min(j + C::NSTAGE, n_tiles - 1), KW);
-    dma(vg, min(j + C::NSTAGE - 1, n_tiles - 1), VW);
+    dma(kg, tile_at(min(j + C::NSTAGE, n_tiles - 1)), KW);
+    dma(vg, tile_at(min(j + C::NSTAGE - 1, n_tiles - 1)), VW);
 
     float neg_m[QB], lsum[QB], mx[QB], m_spec[QB], a_spec[QB];
 #pragma unroll
@@ -461,7 +522,8 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
       lsum[qb] = 0.0f;
       mx[qb] = -__builtin_inff();
     }
-    const bool mask_next = needs_mask(j + 1);
+    const int tile_next = tile_at(j + 1);
+    const bool mask_next = needs_mask(tile_next);
     bool any_alpha = false;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) any_alpha |= alpha[qb] != 1.0f;
@@ -547,7 +609,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) l_run[qb] += lsum[qb];
     if (mask_next) {  // diagonal or ragged tile: mask, then take the row max again
-      mask_tile(s_nxt, j + 1);
+      mask_tile(s_nxt, tile_next);
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         float m = -__builtin_inff();
@@ -627,7 +689,8 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qw0 + 32 * qb + n;
     const float l_tot = wave_sum_halves(l_run[qb]);
-    const float inv = 1.0f / l_tot;
+    float inv = 1.0f / l_tot;
+    if constexpr (C::SPARSE) inv = l_tot > 0.0f ? inv : 0.0f;  // a row that saw no key: O = 0
     if (row < T) {
       char* orow = reinterpret_cast<char*>(o + head_off + (int64_t)row * D);
 #pragma unroll
@@ -641,7 +704,9 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
           *reinterpret_cast<u32x4*>(orow + ((D / 2) * hf + 16 * cb + 8 * half) * 2) = out;
         }
       }
-      if (hf == 0) lse[(int64_t)bh * T + row] = (m_run[qb] + __log2f(l_tot)) * kLn2;
+      float lse_row = (m_run[qb] + __log2f(l_tot)) * kLn2;
+      if constexpr (C::SPARSE) lse_row = l_tot > 0.0f ? lse_row : -__builtin_inff();
+      if (hf == 0) lse[(int64_t)bh * T + row] = lse_row;
     }
   }
 }

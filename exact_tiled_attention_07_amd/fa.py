@@ -55,6 +55,8 @@ def lib():
     L.fa_fwd_ex.restype = i
     L.fa_fwd_plan.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(PlanInfo)]
     L.fa_fwd_plan.restype = i
+    L.fa_fwd_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, vp]
+    L.fa_fwd_sparse.restype = i
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     L.fa_bwd.restype = i
     L.fa_strerror.argtypes = [i]
@@ -204,3 +206,39 @@ def bwd(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None, 
                             delta.data_ptr(), B, H, T, d, int(bool(causal)), scale,
                             _stream_handle(q.device, stream)))
     return dq, dk, dv, delta
+
+
+SPARSE_BLOCK_M = 128  # FA_SPARSE_BLOCK_M: query rows per mask block
+SPARSE_BLOCK_N = 64   # FA_SPARSE_BLOCK_N: keys per mask block
+
+
+def sparse_mask_shape(T: int, mask_heads: int = 1):
+    """Shape of the block mask ``fwd_sparse`` takes for sequence length T."""
+    return (mask_heads, -(-T // SPARSE_BLOCK_M), -(-T // SPARSE_BLOCK_N))
+
+
+def fwd_sparse(q, k, v, block_mask, causal: bool = True, scale: float | None = None, out=None,
+               lse=None, stream=None):
+    """Block-sparse attention forward (``fa_fwd_sparse``): returns ``(o, lse)``.
+
+    ``block_mask`` is a contiguous uint8 GPU tensor ``[mask_heads, ceil(T/128), ceil(T/64)]`` with
+    ``mask_heads`` 1 or B*H; nonzero blocks are computed, the others skipped. Rows with no visible
+    key get o = 0 and lse = -inf.
+    """
+    import torch
+
+    _check_inputs(q, k, v)
+    out, lse = _outputs(q, out, lse)
+    B, H, T, d = q.shape
+    if (not isinstance(block_mask, torch.Tensor) or block_mask.dtype != torch.uint8
+            or not block_mask.is_contiguous() or block_mask.device != q.device):
+        raise TypeError("block_mask must be a contiguous uint8 tensor on q's device")
+    mh = block_mask.shape[0] if block_mask.dim() == 3 else -1
+    if mh not in (1, B * H) or tuple(block_mask.shape) != sparse_mask_shape(T, mh):
+        raise ValueError(f"block_mask must be {sparse_mask_shape(T, 1)} or {sparse_mask_shape(T, B * H)}")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        _check(lib().fa_fwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), B, H, T, d, int(bool(causal)), scale,
+                                   block_mask.data_ptr(), mh, _stream_handle(q.device, stream)))
+    return out, lse

@@ -102,6 +102,31 @@ int fa_fwd_plan(int B, int H, int T, int d, int causal, int block_m, int block_n
                 fa_plan_info* out);
 
 /*
+ * fa_fwd_sparse — exact attention forward under a block mask (block-sparse attention).
+ *
+ * The keys are split into blocks per (query block, key block), and a block whose mask is zero is
+ * skipped as a whole, computing nothing, the way the causal mask skips the blocks above the
+ * diagonal (cnblogs "内核案例研究：Flash Attention", section "块稀疏注意力 V2 和 V3"). Key j is
+ * visible to query i iff
+ *     block_mask[m][i / FA_SPARSE_BLOCK_M][j / FA_SPARSE_BLOCK_N] != 0   (and j <= i if causal),
+ * with m = 0 when mask_heads == 1 and m = b*H + h when mask_heads == B*H. O and LSE are the exact
+ * softmax over the visible keys, as for fa_fwd; a row with no visible key gets O = 0 and
+ * LSE = -inf.
+ *   block_mask [in] uint8 [mask_heads, ceil(T / FA_SPARSE_BLOCK_M), ceil(T / FA_SPARSE_BLOCK_N)],
+ *                   device; nonzero = the block is computed
+ *   mask_heads      1 (one mask for every batch and head) or B*H (one per head)
+ *   T               <= FA_SPARSE_MAX_T
+ *   other arguments, layouts, ownership and errors as for fa_fwd (d = 64 or 128); o and lse must
+ *   not overlap the mask either. FA_ERR_INVALID_ARG for a bad mask_heads or T.
+ */
+#define FA_SPARSE_BLOCK_M 128
+#define FA_SPARSE_BLOCK_N 64
+#define FA_SPARSE_MAX_T 65536
+int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int T, int d, int causal, float scale, const unsigned char* block_mask,
+                  int mask_heads, void* stream);
+
+/*
  * fa_bwd — exact attention backward (gradients of fa_fwd), by recomputation from the saved LSE.
  *
  *     dV = P^T dO,  dP = dO V^T,  D_i = dO_i . O_i,  dS = P o (dP - D),

@@ -21,7 +21,7 @@ def call(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=1, T=8, d=64, causal=
 
 def test_library_exports_every_declared_function():
     names = fa.header_functions()
-    assert names == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_fwd_plan", "fa_strerror"]
+    assert names == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_fwd_plan", "fa_fwd_sparse", "fa_strerror"]
     lib = fa.lib()
     for n in names:
         assert hasattr(lib, n)
@@ -176,3 +176,24 @@ def test_bwd_empty_problem_is_ok(shape):
     B, H, T, d = shape
     assert call_bwd(B=B, H=H, T=T, d=d) == fa.FA_OK
     assert call_bwd(B=B, H=H, T=T, d=d, causal=0) == fa.FA_OK
+
+
+# ---- fa_fwd_sparse: checks before anything is launched
+def call_sparse(B=1, H=1, T=8, d=64, causal=1, scale=0.125, mask=6 * A, mask_heads=1, **kw):
+    p = dict(dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A), **kw)
+    return fa.lib().fa_fwd_sparse(p["q"], p["k"], p["v"], p["o"], p["lse"], B, H, T, d, causal, scale,
+                                  mask, mask_heads, None)
+
+
+def test_sparse_checks():
+    assert call_sparse(mask=None) == fa.FA_ERR_NULL
+    assert call_sparse(o=None) == fa.FA_ERR_NULL
+    assert call_sparse(d=96) == fa.FA_ERR_UNSUPPORTED_D
+    assert call_sparse(T=65537) == fa.FA_ERR_INVALID_ARG      # above FA_SPARSE_MAX_T
+    assert call_sparse(mask_heads=2) == fa.FA_ERR_INVALID_ARG  # neither 1 nor B*H
+    assert call_sparse(B=2, H=3, mask_heads=6, T=0) == fa.FA_OK
+    assert call_sparse(scale=0.0) == fa.FA_ERR_INVALID_ARG
+    assert call_sparse(q=A + 8) == fa.FA_ERR_ALIGNMENT
+    assert call_sparse(o=6 * A) == fa.FA_ERR_INVALID_ARG      # output over the mask
+    assert call_sparse(T=0) == fa.FA_OK and call_sparse(T=0, d=128, causal=0) == fa.FA_OK
+    assert fa.sparse_mask_shape(1000, 1) == (1, 8, 16) and fa.sparse_mask_shape(64, 12) == (12, 1, 1)
