@@ -90,3 +90,17 @@ WORKLOADS = {
     "c5a": Workload("c5a_causal_B4_H12_T16384_d64", 4, 12, 16384, 64, True, seed=5),
     "c5b": Workload("c5b_noncausal_B4_H16_T8192_d128", 4, 16, 8192, 128, False, seed=6),
 }
+
+
+def make_partials(n: int, B: int, H: int, T: int, d: int, seed: int, lse_sigma: float = 4.0,
+                  p_empty: float = 0.1):
+    """Draw synthetic partial results for a merge: ``o_parts`` float32 ``[n, B, H, T, d]`` and
+    ``lse_parts`` float32 ``[n, B, H, T]`` from ``Generator(PCG64(seed))`` (o, then lse, then the
+    empty flags). A fraction ``p_empty`` of the parts is empty: LSE = -inf and O = 0."""
+    gen = np.random.Generator(np.random.PCG64(seed))
+    o = gen.standard_normal((n, B, H, T, d), dtype=np.float32)
+    lse = gen.standard_normal((n, B, H, T), dtype=np.float32) * np.float32(lse_sigma)
+    empty = gen.random((n, B, H, T)) < p_empty
+    lse[empty] = -np.inf
+    o[empty] = 0.0
+    return o, lse

@@ -25,9 +25,15 @@ is zero are not visible, the way the causal mask hides the blocks above the diag
 "内核案例研究：Flash Attention", section "块稀疏注意力 V2 和 V3"); a row with no visible key gets
 ``O = 0`` and ``LSE = -inf``.
 
-Every function here is pinned by the ``not gpu`` tests in ``tests/test_oracle_pins.py`` and
-``tests/test_oracle_bwd_pins.py`` and ``tests/test_oracle_sparse_pins.py`` against closed forms, invariants, finite differences and library
-special cases.
+Two functions are numpy float64 rather than C: ``merge_partials``, the log-space combine of partial
+results over disjoint key ranges (ijyty.com FlashAttention article, section 2.1), and
+``attention_fwd_cross``, the plain two-pass attention of T queries over a key range of a Tk-key
+sequence (one library matmul per head for the scores and one for P V).
+
+Every function here is pinned by the ``not gpu`` tests in ``tests/test_oracle_pins.py``,
+``tests/test_oracle_bwd_pins.py``, ``tests/test_oracle_sparse_pins.py`` and
+``tests/test_oracle_splitkv_pins.py`` against closed forms, invariants, finite differences, brute
+force and library special cases.
 """
 from __future__ import annotations
 
@@ -255,4 +261,90 @@ def attention_fwd_blockmask(q_bits, k_bits, v_bits, causal: bool, scale: float, 
                                       block_n, int(num_threads))
     if rc != 0:
         raise RuntimeError(f"fa_ref_fwd_blockmask failed with code {rc}")
+    return o, lse
+
+
+def merge_partials(o_parts, lse_parts):
+    """Log-space combine of partial results over disjoint key ranges, in float64.
+
+    ``LSE = log sum_s exp(LSE_s)`` and ``O = sum_s exp(LSE_s - LSE) O_s`` (ijyty.com FlashAttention
+    article, section 2.1: the per-block logsumexp accumulated in log space and the output divided by
+    exp(lse) at the end). Parts with LSE_s = -inf contribute nothing; rows whose parts are all -inf
+    get O = 0 and LSE = -inf. ``o_parts`` ``[n, ..., d]``, ``lse_parts`` ``[n, ...]``.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    m = lse_parts.max(axis=0)
+    empty = np.isneginf(m)
+    m_safe = np.where(empty, 0.0, m)
+    w = np.exp(lse_parts - m_safe[None])          # exp(-inf) = 0 for empty parts
+    l = w.sum(axis=0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        o = (w[..., None] * o_parts).sum(axis=0) / np.where(empty, 1.0, l)[..., None]
+        lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, l)))
+    o[empty] = 0.0
+    return o, lse
+
+
+def attention_fwd_key_range(q_bits, k_bits, v_bits, causal: bool, scale: float, k_begin: int,
+                            k_end: int, num_threads: int = 0):
+    """Attention of every query over the keys [k_begin, k_end) only (k_begin a multiple of 64, k_end
+    a multiple of 64 or T): the block-sparse oracle with one query block and the range's 64-key
+    blocks. Returns ``(o, lse)`` float64; rows with no visible key get 0 and -inf."""
+    T = q_bits.shape[2]
+    nk = -(-T // 64)
+    mask = np.zeros((1, 1, nk), dtype=np.uint8)
+    mask[0, 0, k_begin // 64:-(-k_end // 64)] = 1
+    return attention_fwd_blockmask(q_bits, k_bits, v_bits, causal, scale, mask, max(T, 1), 64,
+                                   num_threads)
+
+
+def _bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float64, exactly (a bf16 value is the top half of a float32)."""
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def attention_fwd_cross(q_bits, k_bits, v_bits, causal: bool, scale: float, k_begin: int = 0,
+                        k_end: int | None = None):
+    """Exact attention of T queries over the keys [k_begin, k_end) of a sequence of Tk keys, in
+    float64 with numpy (q ``[B, H, T, d]``, k and v ``[B, H, Tk, d]``, bf16 bit patterns).
+
+    The plain two-pass definition, as in ``fa_ref.c``, for every row: the scores ``scale * q_i . k_j``
+    of the visible keys, their maximum, the exponentials and their sum, then ``O = sum e_j v_j / l``
+    and ``LSE = m + ln l``. With the causal mask the queries are the last T positions of the keys'
+    sequence (keys held for earlier positions, as when decoding after a prefix), so query i sees
+    key j iff ``j <= i + Tk - T``; the pages treat only T = Tk, where this is the usual ``j <= i``
+    (learn-llm.fim.ai "手写 FlashAttention：拆开 SDPA 这个黑盒", STEP 3). A row with no visible key
+    gets ``O = 0`` and ``LSE = -inf``. Returns ``(o, lse)`` float64.
+    """
+    q = _as_bf16_bits(q_bits, "q")
+    k = _as_bf16_bits(k_bits, "k")
+    v = _as_bf16_bits(v_bits, "v")
+    B, H, T, d = q.shape
+    Tk = k.shape[2]
+    if k.shape != v.shape or k.shape[:2] != (B, H) or k.shape[3] != d:
+        raise ValueError(f"k, v must be [B, H, Tk, d] like q: {q.shape} {k.shape} {v.shape}")
+    k_end = Tk if k_end is None else k_end
+    if not (0 <= k_begin <= k_end <= Tk):
+        raise ValueError(f"key range [{k_begin}, {k_end}) outside [0, {Tk})")
+    j = np.arange(Tk)[None, :]
+    i = np.arange(T)[:, None]
+    visible = (j >= k_begin) & (j < k_end)
+    if causal:
+        visible = visible & (j <= i + (Tk - T))
+    o = np.zeros((B, H, T, d))
+    lse = np.full((B, H, T), -np.inf)
+    has_key = visible.any(axis=1)
+    for b in range(B):
+        for h in range(H):
+            qf, kf, vf = (_bf16_to_f64(x[b, h]) for x in (q, k, v))
+            s = float(scale) * (qf @ kf.T)
+            s = np.where(visible, s, -np.inf)
+            m = s.max(axis=1, initial=-np.inf)
+            m_safe = np.where(has_key, m, 0.0)
+            e = np.exp(s - m_safe[:, None])            # exp(-inf) = 0 for hidden keys
+            l = e.sum(axis=1)
+            l_safe = np.where(has_key, l, 1.0)
+            o[b, h] = np.where(has_key[:, None], (e @ vf) / l_safe[:, None], 0.0)
+            lse[b, h] = np.where(has_key, m_safe + np.log(l_safe), -np.inf)
     return o, lse
