@@ -34,6 +34,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 KERNEL_SOURCES = ["exact_tiled_attention_07_amd/csrc/fa_kernel.hpp",
                   "exact_tiled_attention_07_amd/csrc/fa_api.hip"]
 BWD_FLOPS_PER_FWD = 2.5  # the usual count: the backward's matrix products are 2.5x the forward's
@@ -245,6 +246,96 @@ def time_sparse(wl, steps, warmup, density=0.25):
             "dense_ms": round(ms_dense, 5), "speedup_vs_dense": round(ms_dense / ms_sparse, 3)}
 
 
+def _event_timer(stream, steps, warmup):
+    import torch
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize(stream.device)
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+        for i in range(steps):
+            starts[i].record(stream)
+            fn()
+            ends[i].record(stream)
+        torch.cuda.synchronize(stream.device)
+        return sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / steps
+    return timed
+
+
+# Decode-shaped split-KV workloads: a few new queries per sequence at the end of the 16384-key
+# sequences of the B=4, H=12, d=64 workload (causal, the queries after the keys' prefix).
+DECODE_SHAPES = ((4, 12, 1, 16384, 64), (4, 12, 16, 16384, 64))
+
+
+def time_splitkv(steps, warmup):
+    """fa_fwd_splitkv on decode shapes (vs one range, i.e. no split), and the T=16384 workload cut
+    into 4 key shards (fa_fwd_partial x4 + fa_merge) vs fa_fwd. Returns the bench line's object."""
+    import torch
+
+    import exact_tiled_attention_07_amd as fa
+    from exact_tiled_attention_07_amd.inputs import WORKLOADS, make_qkv, to_torch_bf16
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    timed = _event_timer(stream, steps, warmup)
+    decode = []
+    for (B, H, T, Tk, d) in DECODE_SHAPES:
+        q = to_torch_bf16(make_qkv(B, H, T, d, seed=91)[0], dev)
+        _, kb, vb = make_qkv(B, H, Tk, d, seed=92)
+        k, v = to_torch_bf16(kb, dev), to_torch_bf16(vb, dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+        n = fa.splitkv_splits(B, H, T, Tk, d)
+        ws = torch.empty(fa.splitkv_workspace_bytes(B, H, T, d, n), dtype=torch.uint8, device=dev)
+        ms = timed(lambda: fa.fwd_splitkv(q, k, v, causal=True, n_splits=n, out=o, lse=lse, workspace=ws,
+                                          stream=stream))
+        ms1 = timed(lambda: fa.fwd_splitkv(q, k, v, causal=True, n_splits=1, out=o, lse=lse, workspace=ws,
+                                           stream=stream))
+        # algorithmic HBM bytes: q, k, v read once, o and lse written once (the partial results'
+        # round trip through the workspace is the split's own cost, so it is not counted)
+        alg = B * H * (2 * T * d * 2 + 2 * Tk * d * 2 + T * 4)
+        gbs = alg / (ms * 1e-3) / 1e9
+        decode.append({"shape": f"B{B} H{H} T{T} Tk{Tk} d{d} causal", "n_splits": n,
+                       "ms_per_step": round(ms, 5), "no_split_ms": round(ms1, 5),
+                       "speedup_vs_no_split": round(ms1 / ms, 3),
+                       "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                                    "traffic": None, "algorithmic_bytes": alg}})
+        del ws
+    wl = WORKLOADS["c5a"]
+    q, k, v = (to_torch_bf16(x, dev) for x in wl.make())
+    o, lse = torch.empty_like(q), torch.empty((wl.B, wl.H, wl.T), dtype=torch.float32, device=dev)
+    shards = 4
+    edges = [wl.T * i // shards for i in range(shards + 1)]
+    op = torch.empty((shards, wl.B, wl.H, wl.T, wl.d), dtype=torch.float32, device=dev)
+    lp = torch.empty((shards, wl.B, wl.H, wl.T), dtype=torch.float32, device=dev)
+
+    def sharded():
+        for i in range(shards):
+            fa.fwd_partial(q, k, v, edges[i], edges[i + 1], causal=True, scale=wl.scale, o_part=op[i],
+                           lse_part=lp[i], stream=stream)
+        fa.merge(op, lp, out=o, lse=lse, stream=stream)
+
+    few = max(3, steps // 10), max(2, warmup // 10)
+    timed_few = _event_timer(stream, *few)
+    ms_sh = timed_few(sharded)
+    ms_merge = timed_few(lambda: fa.merge(op, lp, out=o, lse=lse, stream=stream))
+    ms_dense = timed_few(lambda: fa.fwd(q, k, v, causal=True, scale=wl.scale, out=o, lse=lse, stream=stream))
+    rows = wl.B * wl.H * wl.T
+    merge_bytes = shards * rows * (wl.d + 1) * 4 + rows * (wl.d * 2 + 4)
+    mgbs = merge_bytes / (ms_merge * 1e-3) / 1e9
+    del op, lp
+    return {"decode": decode,
+            "key_shards": {"workload": wl.name, "shards": shards, "ms_per_step": round(ms_sh, 5),
+                           "tflops": round(wl.flops / (ms_sh * 1e-3) / 1e12, 2), "dense_ms": round(ms_dense, 5),
+                           "overhead_vs_dense": round(ms_sh / ms_dense, 3), "merge_ms": round(ms_merge, 5),
+                           "merge_roofline": {"bound": "hbm", "achieved": round(mgbs, 1), "peak": PEAK_HBM_GBS,
+                                              "unit": "GB/s", "frac": round(mgbs / PEAK_HBM_GBS, 4),
+                                              "traffic": None, "algorithmic_bytes": merge_bytes}}}
+
+
 def cpu_baseline(wl, budget_s=20.0):
     """Time the CPU oracle on a bounded sample of the workload (whole heads, all host cores)."""
     import numpy as np
@@ -302,6 +393,7 @@ def main(argv=None):
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-sparse", action="store_true")
+    ap.add_argument("--no-splitkv", action="store_true")
     ap.add_argument("--only-backward", action="store_true",
                     help="time fa_bwd only and print its line (for profiling the backward)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -365,6 +457,11 @@ def main(argv=None):
         sparse = time_sparse(WORKLOADS["c5a"], max(5, args.steps // 10), max(2, args.warmup // 10))
         print(f"[bench] sparse: {sparse}", file=sys.stderr, flush=True)
 
+    splitkv = None
+    if not args.no_splitkv:
+        splitkv = time_splitkv(args.steps, args.warmup)
+        print(f"[bench] splitkv: {splitkv}", file=sys.stderr, flush=True)
+
     copy_calibration(args.copy_calibration_mib)
 
     base = None
@@ -403,6 +500,7 @@ def main(argv=None):
         "sweep": sweep,
         "backward": backward,
         "sparse": sparse,
+        "splitkv": splitkv,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -9,11 +9,12 @@
 #include "fa.h"
 #include "fa_bwd_kernel.hpp"
 #include "fa_kernel.hpp"
+#include "fa_merge_kernel.hpp"
 
 namespace {
 
 using KernelFn = void (*)(const __bf16*, const __bf16*, const __bf16*, __bf16*, float*, int, int, int,
-                          float, const uint8_t*, int);
+                          float, const uint8_t*, int, int, int, int, int);
 
 struct TileEntry {
   int d, block_m, block_n, waves;
@@ -102,7 +103,7 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
   KernelFn fn = causal ? tile->causal_fn : tile->full_fn;
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * tile->waves), 0, (hipStream_t)stream,
                      (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, T, nq, BH,
-                     scale_log2, (const uint8_t*)nullptr, 0);
+                     scale_log2, (const uint8_t*)nullptr, 0, 0, 0, 0, 0);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }
@@ -148,9 +149,159 @@ int launch_sparse(const void* q, const void* k, const void* v, void* o, float* l
   else fn = causal ? &fa::fa_fwd_kernel<SparseFns<128>::Cc> : &fa::fa_fwd_kernel<SparseFns<128>::Cf>;
   hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, (const __bf16*)q,
                      (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, T, nq, BH,
-                     scale * fa::kLog2e, (const uint8_t*)block_mask, mask_heads);
+                     scale * fa::kLog2e, (const uint8_t*)block_mask, mask_heads, 0, 0, 0, 0);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
+}
+
+// Partial forward over a key range: the default tile with the range selection and fp32 output.
+template <int D>
+struct RangeFns {
+  using Cc = fa::Cfg<D, 1, 4, 64, true, 2, false, true>;
+  using Cf = fa::Cfg<D, 1, 4, 64, false, 2, false, true>;
+  // fewer queries than one workgroup's 128: the idle waves skip the arithmetic
+  using CcFew = fa::Cfg<D, 1, 4, 64, true, 2, false, true, true>;
+  using CfFew = fa::Cfg<D, 1, 4, 64, false, 2, false, true, true>;
+  static_assert(Cc::BN == FA_PARTIAL_KEY_ALIGN, "key ranges start on tile boundaries");
+  static_assert(CcFew::BM == Cc::BM, "same workgroup shape");
+};
+
+// Checks shared by the key-range entry points: sizes, the query/key lengths and the alignment of q,
+// k, v and the fp32 partial outputs. `parts` partial results of B*H*T rows are written.
+int check_partial_args(const void* q, const void* k, const void* v, const float* o_part,
+                       const float* lse_part, int B, int H, int T, int Tk, int d, float scale,
+                       int64_t parts) {
+  if (!q || !k || !v || !o_part || !lse_part) return FA_ERR_NULL;
+  int rc = check_sizes(B, H, T, d);
+  if (rc != FA_OK) return rc;
+  if (Tk < 0 || Tk > FA_MAX_T) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o_part) & 15u) return FA_ERR_ALIGNMENT;
+  if ((uintptr_t)lse_part & 3u) return FA_ERR_ALIGNMENT;
+  const size_t rows = (size_t)B * H * T, krows = (size_t)B * H * Tk;
+  const size_t qbytes = rows * d * 2, kbytes = krows * d * 2;
+  const size_t obytes = (size_t)parts * rows * d * 4, lse_bytes = (size_t)parts * rows * 4;
+  const void* ins[3] = {q, k, v};
+  const size_t in_bytes[3] = {qbytes, kbytes, kbytes};
+  for (int a = 0; a < 3; ++a)
+    if (overlaps(o_part, obytes, ins[a], in_bytes[a]) || overlaps(lse_part, lse_bytes, ins[a], in_bytes[a]))
+      return FA_ERR_INVALID_ARG;
+  if (overlaps(o_part, obytes, lse_part, lse_bytes)) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+// One launch of the key-range kernel: grid x = (Q block, head), grid y = n_splits key ranges of
+// k_chunk keys from k_begin (the last one ends at k_end); range s writes partial result s.
+int launch_ranges(const void* q, const void* k, const void* v, float* o_part, float* lse_part, int B,
+                  int H, int T, int Tk, int d, int causal, float scale, int k_begin, int k_end,
+                  int k_chunk, int n_splits, void* stream) {
+  const int nq = (T + 127) / 128;
+  const int BH = B * H;
+  const int64_t grid = (int64_t)nq * BH;
+  if (grid > 0x7fffffffLL || n_splits > 65535) return FA_ERR_INVALID_ARG;
+  const bool few = T < RangeFns<64>::Cc::BM;
+  KernelFn fn;
+  if (d == 64)
+    fn = few ? (causal ? &fa::fa_fwd_kernel<RangeFns<64>::CcFew> : &fa::fa_fwd_kernel<RangeFns<64>::CfFew>)
+             : (causal ? &fa::fa_fwd_kernel<RangeFns<64>::Cc> : &fa::fa_fwd_kernel<RangeFns<64>::Cf>);
+  else
+    fn = few ? (causal ? &fa::fa_fwd_kernel<RangeFns<128>::CcFew> : &fa::fa_fwd_kernel<RangeFns<128>::CfFew>)
+             : (causal ? &fa::fa_fwd_kernel<RangeFns<128>::Cc> : &fa::fa_fwd_kernel<RangeFns<128>::Cf>);
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid, (unsigned)n_splits), dim3(256), 0, (hipStream_t)stream,
+                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o_part, lse_part, T,
+                     nq, BH, scale * fa::kLog2e, (const uint8_t*)nullptr, 0, k_begin, k_end, Tk, k_chunk);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+int launch_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part, int B,
+                   int H, int T, int Tk, int d, int causal, float scale, int k_begin, int k_end,
+                   void* stream) {
+  int rc = check_partial_args(q, k, v, o_part, lse_part, B, H, T, Tk, d, scale, 1);
+  if (rc != FA_OK) return rc;
+  if (k_begin < 0 || k_end < k_begin || k_end > Tk || k_begin % FA_PARTIAL_KEY_ALIGN != 0 ||
+      (k_end % FA_PARTIAL_KEY_ALIGN != 0 && k_end != Tk))
+    return FA_ERR_INVALID_ARG;
+  if ((size_t)B * H * T == 0) return FA_OK;
+  return launch_ranges(q, k, v, o_part, lse_part, B, H, T, Tk, d, causal, scale, k_begin, k_end,
+                       std::max(k_end - k_begin, 1), 1, stream);
+}
+
+// Keys per range when Tk keys are split n_splits ways: equal ranges of whole 64-key tiles.
+int split_chunk(int Tk, int n_splits) {
+  const int tiles = (Tk + FA_PARTIAL_KEY_ALIGN - 1) / FA_PARTIAL_KEY_ALIGN;
+  const int per = std::max(1, (tiles + n_splits - 1) / n_splits);
+  return per * FA_PARTIAL_KEY_ALIGN;
+}
+
+int splits_used(int Tk, int n_splits) {
+  const int chunk = split_chunk(Tk, n_splits);
+  return std::max(1, (Tk + chunk - 1) / chunk);
+}
+
+int launch_merge_kernel(const float* o_parts, const float* lse_parts, int n_parts, void* o, float* lse,
+                        int64_t rows, int d, void* stream);
+
+int launch_merge(const float* o_parts, const float* lse_parts, int n_parts, void* o, float* lse,
+                 int B, int H, int T, int d, void* stream) {
+  if (!o_parts || !lse_parts || !o || !lse) return FA_ERR_NULL;
+  int rc = check_sizes(B, H, T, d);
+  if (rc != FA_OK) return rc;
+  if (n_parts < 1 || n_parts > FA_MERGE_MAX_PARTS) return FA_ERR_INVALID_ARG;
+  if ((((uintptr_t)o_parts | (uintptr_t)o) & 15u) || ((uintptr_t)lse_parts | (uintptr_t)lse) & 3u)
+    return FA_ERR_ALIGNMENT;
+  const int64_t rows = (int64_t)B * H * T;
+  const size_t pbytes = (size_t)n_parts * rows * d * 4, plbytes = (size_t)n_parts * rows * 4;
+  const size_t obytes = (size_t)rows * d * 2, lbytes = (size_t)rows * 4;
+  if (overlaps(o, obytes, o_parts, pbytes) || overlaps(o, obytes, lse_parts, plbytes) ||
+      overlaps(lse, lbytes, o_parts, pbytes) || overlaps(lse, lbytes, lse_parts, plbytes) ||
+      overlaps(o, obytes, lse, lbytes))
+    return FA_ERR_INVALID_ARG;
+  if (rows == 0) return FA_OK;
+  return launch_merge_kernel(o_parts, lse_parts, n_parts, o, lse, rows, d, stream);
+}
+
+int launch_merge_kernel(const float* o_parts, const float* lse_parts, int n_parts, void* o, float* lse,
+                        int64_t rows, int d, void* stream) {
+  const int rpb = 256 / (d / 4);
+  const int64_t grid = (rows + rpb - 1) / rpb;
+  if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  auto fn = d == 64 ? &fa::fa_merge_kernel<64> : &fa::fa_merge_kernel<128>;
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, o_parts, lse_parts,
+                     n_parts, (__bf16*)o, lse, rows);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+int launch_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int T, int Tk, int d, int causal, float scale, int n_splits, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!o || !lse || !workspace) return FA_ERR_NULL;
+  if (n_splits < 1 || n_splits > FA_MERGE_MAX_PARTS) return FA_ERR_INVALID_ARG;
+  int rc = check_sizes(B, H, T, d);
+  if (rc != FA_OK) return rc;
+  const size_t need = fa_splitkv_workspace_bytes(B, H, T, d, n_splits);
+  if (workspace_bytes < need || (need == 0 && (size_t)B * H * T != 0)) return FA_ERR_INVALID_ARG;
+  const int64_t rows = (int64_t)B * H * T;
+  float* o_parts = static_cast<float*>(workspace);
+  float* lse_parts = o_parts + (size_t)n_splits * rows * d;
+  rc = check_partial_args(q, k, v, o_parts, lse_parts, B, H, T, Tk, d, scale, n_splits);
+  if (rc != FA_OK) return rc;
+  if (((uintptr_t)o & 15u) || ((uintptr_t)lse & 3u)) return FA_ERR_ALIGNMENT;
+  const size_t obytes = (size_t)rows * d * 2, lbytes = (size_t)rows * 4;
+  const void* ins[4] = {q, k, v, workspace};
+  const size_t in_bytes[4] = {(size_t)rows * d * 2, (size_t)B * H * Tk * d * 2, (size_t)B * H * Tk * d * 2,
+                              need};
+  for (int a = 0; a < 4; ++a)
+    if (overlaps(o, obytes, ins[a], in_bytes[a]) || overlaps(lse, lbytes, ins[a], in_bytes[a]))
+      return FA_ERR_INVALID_ARG;
+  if (overlaps(o, obytes, lse, lbytes)) return FA_ERR_INVALID_ARG;
+  if (rows == 0) return FA_OK;
+  const int used = splits_used(Tk, n_splits);
+  rc = launch_ranges(q, k, v, o_parts, lse_parts, B, H, T, Tk, d, causal, scale, 0, Tk,
+                     split_chunk(Tk, n_splits), used, stream);
+  if (rc != FA_OK) return rc;
+  return launch_merge_kernel(o_parts, lse_parts, used, o, lse, rows, d, stream);
 }
 
 int launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -208,6 +359,42 @@ int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* l
                   int T, int d, int causal, float scale, const unsigned char* block_mask,
                   int mask_heads, void* stream) {
   return launch_sparse(q, k, v, o, lse, B, H, T, d, causal, scale, block_mask, mask_heads, stream);
+}
+
+int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                   int B, int H, int T, int Tk, int d, int causal, float scale, int k_begin, int k_end,
+                   void* stream) {
+  return launch_partial(q, k, v, o_part, lse_part, B, H, T, Tk, d, causal, scale, k_begin, k_end,
+                        stream);
+}
+
+size_t fa_splitkv_workspace_bytes(int B, int H, int T, int d, int n_splits) {
+  if (B < 0 || H < 0 || T < 0 || d < 0 || n_splits < 1) return 0;
+  const size_t per_part = (size_t)B * H * T * ((size_t)d + 1) * 4;  // B*H*T <= 2^46: no overflow
+  if (per_part > SIZE_MAX / (size_t)n_splits) return 0;
+  return (size_t)n_splits * per_part;
+}
+
+int fa_splitkv_splits(int B, int H, int T, int Tk, int d) {
+  if (B <= 0 || H <= 0 || T <= 0 || Tk <= 0 || (d != 64 && d != 128)) return 1;
+  // as many workgroups as two per compute unit hold at once (not more: a second round would wait
+  // for the first), with at least 8 key tiles (512 keys) per range
+  const int64_t base = (int64_t)((T + 127) / 128) * B * H;
+  const int64_t want = 512 / base;
+  const int64_t most = std::max(1, ((Tk + FA_PARTIAL_KEY_ALIGN - 1) / FA_PARTIAL_KEY_ALIGN) / 8);
+  return (int)std::max<int64_t>(1, std::min<int64_t>({want, most, FA_MERGE_MAX_PARTS}));
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int T, int Tk, int d, int causal, float scale, int n_splits, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return launch_splitkv(q, k, v, o, lse, B, H, T, Tk, d, causal, scale, n_splits, workspace,
+                        workspace_bytes, stream);
+}
+
+int fa_merge(const float* o_parts, const float* lse_parts, int n_parts, void* o, float* lse, int B,
+             int H, int T, int d, void* stream) {
+  return launch_merge(o_parts, lse_parts, n_parts, o, lse, B, H, T, d, stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

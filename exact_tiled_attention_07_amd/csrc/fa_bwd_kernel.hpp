@@ -28,8 +28,6 @@
 
 namespace fa {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 template <int D_, bool CAUSAL_>
 struct BwdCfg {
   static constexpr int D = D_;

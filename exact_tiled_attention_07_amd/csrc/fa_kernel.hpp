@@ -52,12 +52,14 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSparseMaxFloor = -1.0e30f;  // running-max floor of the block-sparse path
 
-template <int D_, int QB_, int NW_, int BN_, bool CAUSAL_, int NSTAGE_, bool SPARSE_ = false>
+template <int D_, int QB_, int NW_, int BN_, bool CAUSAL_, int NSTAGE_, bool SPARSE_ = false,
+          bool RANGE_ = false, bool FEWQ_ = false>
 struct Cfg {
   static constexpr int D = D_;        // head dim
   static constexpr int QB = QB_;      // 32-query column blocks per wave
@@ -69,6 +71,13 @@ struct Cfg {
   // indices are compacted into an LDS list (at most MAX_LIST tiles, i.e. T <= MAX_LIST * BN)
   static constexpr bool SPARSE = SPARSE_;
   static constexpr int MAX_LIST = SPARSE_ ? 1024 : 0;
+  // key range: only the tiles of keys [k_begin, k_end) are visited and the outputs are the partial
+  // O (fp32, normalised over the range) and LSE of that range, for a later log-space merge
+  static constexpr bool RANGE = RANGE_;
+  static constexpr bool LISTED = SPARSE_ || RANGE_;  // rows may see no key
+  static_assert(!(SPARSE_ && RANGE_), "one tile selection at a time");
+  // fewer queries than a workgroup holds (T < BM): waves without a query row skip the arithmetic
+  static constexpr bool FEWQ = FEWQ_;
   static constexpr int BM = 32 * QB * NW;           // queries per workgroup
   static constexpr int THREADS = 64 * NW;
   static constexpr int ROW_BYTES = D * 2;           // one bf16 row of K or V
@@ -210,7 +219,8 @@ template <class C>
 __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int T, int nq, int BH, float scale_log2,
-    const uint8_t* __restrict__ bmask, int mask_heads) {
+    const uint8_t* __restrict__ bmask, int mask_heads, int k_begin, int k_end, int t_keys,
+    int k_chunk) {
   constexpr int D = C::D, QB = C::QB, NW = C::NW, BN = C::BN, BM = C::BM;
   constexpr int KB = C::KB, CB = C::CB, PT = C::PT, KSTEPS = C::KSTEPS, RB = C::ROW_BYTES;
   constexpr int NS_QK = C::NS_QK, NS = C::NS, PD = C::PD;
@@ -224,18 +234,39 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   const int hf = lane >> 5;   // which half of the wave (0/1)
   (void)bmask;
   (void)mask_heads;
+  (void)k_begin;
+  (void)k_end;
+  (void)t_keys;
+  (void)k_chunk;
 
   int qblk, bh;
   map_block<C::CAUSAL>(blockIdx.x, nq, BH, qblk, bh);
   const int q0 = qblk * BM;
-  const int64_t head_off = (int64_t)bh * T * D;
-  const char* kg = reinterpret_cast<const char*>(k + head_off);
-  const char* vg = reinterpret_cast<const char*>(v + head_off);
+  // T is the number of queries. A key range may come from a longer sequence of Tk keys (queries
+  // then sit at its end: query i is at key position i + coff, the causal diagonal shifted by coff),
+  // and blockIdx.y picks one of several equal key ranges, each with its own partial output.
+  const int Tk = C::RANGE ? t_keys : T;
+  const int coff = C::RANGE ? Tk - T : 0;
+  if constexpr (C::RANGE) {
+    const int split = blockIdx.y;
+    k_begin += split * k_chunk;
+    k_end = min(k_begin + k_chunk, k_end);
+    o = reinterpret_cast<__bf16*>(reinterpret_cast<float*>(o) + (int64_t)split * BH * T * D);
+    lse += (int64_t)split * BH * T;
+  }
+  const int64_t head_off = (int64_t)bh * T * D;    // q and o rows of this head
+  const int64_t head_off_k = (int64_t)bh * Tk * D;  // k and v rows of this head
+  const char* kg = reinterpret_cast<const char*>(k + head_off_k);
+  const char* vg = reinterpret_cast<const char*>(v + head_off_k);
   const int qw0 = q0 + 32 * QB * w;  // first query of this wave
+  // With few queries (a key range for a handful of new queries) whole waves hold no query row:
+  // they still copy their share of every tile and meet every barrier, but skip the MFMA and the
+  // softmax (a wave-uniform branch; the barriers stay outside it).
+  const bool wave_active = !C::FEWQ || qw0 < T;
 
   // K/V tiles this workgroup needs: up to the diagonal when causal (tiles above it are never
   // touched), all of them otherwise. The last one reaches past T only for a ragged end.
-  const int kv_end = C::CAUSAL ? min(q0 + BM, T) : T;
+  const int kv_end = C::CAUSAL ? max(0, min(q0 + BM + coff, Tk)) : Tk;
   const int n_cand = (kv_end + BN - 1) / BN;  // candidate tiles 0 .. n_cand-1
   // Block-sparse: keep the candidates whose mask byte is nonzero, in ascending order, as a list in
   // LDS; tile_at(x) is the x-th tile visited (the identity when dense).
@@ -266,19 +297,25 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     }
     n_tiles = __builtin_amdgcn_readfirstlane(count);
   }
+  const int t_begin = C::RANGE ? k_begin / BN : 0;  // first tile of the key range
+  if constexpr (C::RANGE) n_tiles = max(0, min((k_end + BN - 1) / BN, n_cand) - t_begin);
+  // (k_begin, k_end and t_begin are uniform; n_tiles stays a scalar)
   auto tile_at = [&](int x) -> int {
     if constexpr (C::SPARSE) return __builtin_amdgcn_readfirstlane((int)tlist[x]);
-    else return x;
+    else return t_begin + x;
   };
-  if constexpr (C::SPARSE) {
+  if constexpr (C::LISTED) {
     if (n_tiles == 0) {  // no key visible to any row of the block: O = 0, LSE = -inf
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int row = qw0 + 32 * qb + n;
         if (row < T) {
-          u32x4* orow = reinterpret_cast<u32x4*>(o + head_off + (int64_t)row * D);
+          u32x4* orow = reinterpret_cast<u32x4*>(
+              C::RANGE ? static_cast<void*>(reinterpret_cast<float*>(o) + head_off + (int64_t)row * D)
+                       : static_cast<void*>(o + head_off + (int64_t)row * D));
+          constexpr int CHUNKS16 = C::RANGE ? D / 4 : D / 8;  // 16-byte chunks of one output row
 #pragma unroll
-          for (int c = 0; c < D / 16; ++c) orow[2 * c + hf] = u32x4{0u, 0u, 0u, 0u};
+          for (int c = 0; c < CHUNKS16 / 2; ++c) orow[2 * c + hf] = u32x4{0u, 0u, 0u, 0u};
           if (hf == 0) lse[(int64_t)bh * T + row] = -__builtin_inff();
         }
       }
@@ -286,11 +323,11 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     }
   }
   const int last_tile = tile_at(n_tiles - 1);
-  const bool tail_ragged = (last_tile + 1) * BN > T;
+  const bool tail_ragged = (last_tile + 1) * BN > Tk;
 
   // ---- HBM -> LDS copies of one K or V tile. Lane `lane` of load i fills 16 bytes of the 1 KiB
-  // LDS region (i*NW + w); it fetches the logical chunk that the swizzle puts there. Rows past T
-  // are clamped to row T-1 (always in bounds); their scores are masked and their V rows zeroed.
+  // LDS region (i*NW + w); it fetches the logical chunk that the swizzle puts there. Rows past Tk
+  // are clamped to row Tk-1 (always in bounds); their scores are masked and their V rows zeroed.
   int dma_row[C::LOADS], dma_col[C::LOADS];
   uint32_t dma_off[C::LOADS];
 #pragma unroll
@@ -302,14 +339,14 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   }
   auto dma = [&](const char* g, int tile, int buf_off) {
     const int kt0 = tile * BN;
-    if (kt0 + BN <= T) {  // whole tile inside the sequence: scalar base + per-lane constant
+    if (kt0 + BN <= Tk) {  // whole tile inside the sequence: scalar base + per-lane constant
       const char* gt = g + (size_t)kt0 * RB;
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) lds_copy16(gt, dma_off[i], lds0 + buf_off + (i * NW + w) * 1024);
     } else {
       // the tile's first and the sequence's last row pass through an empty asm so that the
       // per-lane clamping below stays in this (rare) branch instead of being hoisted into every step
-      int first = kt0, last = T - 1;
+      int first = kt0, last = Tk - 1;
       asm volatile("" : "+s"(first), "+s"(last));
 #pragma unroll
       for (int i = 0; i < C::LOADS; ++i) {
@@ -318,10 +355,10 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
       }
     }
   };
-  // Zero the V rows at or past T of a ragged last tile, so a clamped copy of row T-1 can never
+  // Zero the V rows at or past Tk of a ragged last tile, so a clamped copy of row Tk-1 can never
   // reach the output (their weights are 0; a non-finite input row would still give 0 * inf).
   auto zero_v_tail = [&](int buf_off) {
-    const int first = T - last_tile * BN;  // first row to clear, 0 < first < BN
+    const int first = Tk - last_tile * BN;  // first row to clear, 0 < first < BN
     char* vl = smem + buf_off;
     for (int idx = tid; idx < (BN - first) * C::CHUNKS; idx += C::THREADS) {
       const int r = first + idx / C::CHUNKS;
@@ -399,16 +436,16 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   u32x4 pf[QB][PT];               // bf16 P of the current tile, B operand layout of P.V
 
   // ---- score-tile helpers -----------------------------------------------------------------
-  // Mask tile `tile` of scores in place: key > query (causal) or key >= T become -inf.
+  // Mask tile `tile` of scores in place: key > query + coff (causal) or key >= Tk become -inf.
   // Register r of key block kb holds key kt0 + 4*hf + off with off = 32*kb + 8*(r/4) + r%4, a
-  // compile-time constant. The key is visible iff key <= last, last = min(query, T-1) (causal) or
-  // T-1, so each score needs one compare of the constant against a per-lane bound.
+  // compile-time constant. The key is visible iff key <= last, last = min(query + coff, Tk-1)
+  // (causal) or Tk-1, so each score needs one compare of the constant against a per-lane bound.
   auto mask_tile = [&](f32x16 (&s)[KB][QB], int tile) {
     const int kt0 = tile * BN;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int qi = qw0 + 32 * qb + n;
-      const int last = C::CAUSAL ? min(qi, T - 1) : T - 1;
+      const int last = C::CAUSAL ? min(qi + coff, Tk - 1) : Tk - 1;
       const int bound = last - kt0 - 4 * hf;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
@@ -421,7 +458,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   };
   auto needs_mask = [&](int tile) {
     const int kt0 = tile * BN;
-    return (C::CAUSAL && kt0 + BN - 1 > qw0) || (kt0 + BN > T);
+    return (C::CAUSAL && kt0 + BN - 1 > qw0 + coff) || (kt0 + BN > Tk);
   };
   // One pair of scores -> exp2, fp32 row sum, packed bf16 P. Pair p covers registers 2*(p%8), +1
   // of key block p/8, i.e. element p%4 of P^T k-step p/4.
@@ -483,17 +520,19 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) sa[kb][qb] = f32x16{};
+  if (wave_active) {
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s)
+    for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      const bf16x8 kf = read_k(buf_of(0) * C::TILE_BYTES, kb, s);
+      for (int kb = 0; kb < KB; ++kb) {
+        const bf16x8 kf = read_k(buf_of(0) * C::TILE_BYTES, kb, s);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-        sa[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][s], sa[kb][qb], 0, 0, 0);
-    }
+        for (int qb = 0; qb < QB; ++qb)
+          sa[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][s], sa[kb][qb], 0, 0, 0);
+      }
+  }
   __syncthreads();  // every wave has read K(0) before K(2) is copied into its buffer
-  if (needs_mask(tile_at(0))) mask_tile(sa, tile_at(0));
+  if (wave_active && needs_mask(tile_at(0))) mask_tile(sa, tile_at(0));
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     float mx = -__builtin_inff();
@@ -502,7 +541,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     // block-sparse: a row may see no key of its first tile (or of any); a finite floor keeps
     // exp2(s - m) at 0 for masked scores instead of NaN, and the floor is left behind (with
     // alpha = 0) as soon as the row sees a key
-    if constexpr (C::SPARSE) m_run[qb] = max_f32(m_run[qb], kSparseMaxFloor);
+    if constexpr (C::LISTED) m_run[qb] = max_f32(m_run[qb], kSparseMaxFloor);
   }
 
   // ---- one pipelined step: softmax + P.V of tile j (scores in s_cur, V at LDS offset VR) while
@@ -514,115 +553,117 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     dma(kg, tile_at(min(j + C::NSTAGE, n_tiles - 1)), KW);
     dma(vg, tile_at(min(j + C::NSTAGE - 1, n_tiles - 1)), VW);
 
-    float neg_m[QB], lsum[QB], mx[QB], m_spec[QB], a_spec[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      neg_m[qb] = -m_run[qb];
-      l_run[qb] *= alpha[qb];
-      lsum[qb] = 0.0f;
-      mx[qb] = -__builtin_inff();
-    }
-    const int tile_next = tile_at(j + 1);
-    const bool mask_next = needs_mask(tile_next);
-    bool any_alpha = false;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) any_alpha |= alpha[qb] != 1.0f;
-    const bool need_rescale = __builtin_amdgcn_ballot_w64(any_alpha) != 0;
-
-    // LDS fragment of slot b: one K read (score slots) or two transposing V reads (P.V slots).
-    bf16x8 kfr[NS_QK];
-    s16x4 vfr[C::NS_PV][2];
-    auto issue = [&](auto b_) {
-      constexpr int b = decltype(b_)::value;
-      if constexpr (b < NS_QK) {
-        kfr[b] = read_k(KR, b % KB, b / KB);
-      } else {
-        constexpr int t = (b - NS_QK) / CB, cb = (b - NS_QK) % CB;
-        vfr[b - NS_QK][0] = read_v(VR, t, cb, 0);
-        vfr[b - NS_QK][1] = read_v(VR, t, cb, 1);
-      }
-    };
-    static_for<0, PD>([&](auto b_) { issue(b_); });
-
-    static_for<0, NS>([&](auto b_) {
-      constexpr int b = decltype(b_)::value;
-      // prefetch the fragments of slot b+PD (the compiler waits for slot b's before its MFMA)
-      if constexpr (b + PD < NS) issue(std::integral_constant<int, b + PD>{});
-      if constexpr (b < NS_QK) {
-        constexpr int s = b / KB, kb = b % KB;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
-          s_nxt[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              kfr[b], qf[qb][s], s == 0 ? f32x16{} : s_nxt[kb][qb], 0, 0, 0);
-      } else {
-        constexpr int t = (b - NS_QK) / CB, cb = (b - NS_QK) % CB;
-        pv_mfma(cb, t, vfr[b - NS_QK][0], vfr[b - NS_QK][1]);
-      }
-      // VALU work of this slot: the exp pairs assigned to it ...
-      if constexpr (b < C::EXP_WINDOW) {
-        constexpr int p_lo = (b * C::NPAIRS + C::EXP_WINDOW - 1) / C::EXP_WINDOW;
-        constexpr int p_hi = ((b + 1) * C::NPAIRS + C::EXP_WINDOW - 1) / C::EXP_WINDOW;
-        static_for<p_lo, (p_hi < C::NPAIRS ? p_hi : C::NPAIRS)>([&](auto p_) {
-          constexpr int p = decltype(p_)::value;
-          static_assert(NS_QK + (p / 4) * CB > b, "exp pair scheduled after its P.V slot");
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) exp_pair(s_cur, qb, p, neg_m[qb], lsum[qb]);
-        });
-      }
-      // ... the pending rescale of acc, in the first slot and skipped when no row of the wave has
-      // a new max (alpha is then exactly 1 in every lane: a wave-uniform branch) ...
-      if constexpr (b == 0) {
-        if (need_rescale) {
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) rescale_chunk(qb, 0, 16);
-        }
-      }
-      // ... and, once the next scores are complete, a chunk of their row max, then the new max and
-      // alpha (assuming the tile needs no mask; masked tiles redo this after the slots).
-      if constexpr (b >= C::MAX_FIRST && b <= C::MAX_LAST) {
-        constexpr int nmax = C::MAX_LAST - C::MAX_FIRST + 1;
-        constexpr int r0 = (b - C::MAX_FIRST) * 16 / nmax, r1 = (b - C::MAX_FIRST + 1) * 16 / nmax;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          max_chunk(s_nxt, qb, r0, r1, mx[qb]);
-          // keep the chunk in this slot (otherwise it sinks past the edge-tile branch below)
-          asm volatile("" : "+v"(mx[qb]));
-        }
-      }
-      if constexpr (b == NS - 2) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          m_spec[qb] = new_max(mx[qb], m_run[qb]);
-          asm volatile("" : "+v"(m_spec[qb]));
-        }
-      }
-      if constexpr (b == NS - 1) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          a_spec[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_spec[qb]);
-          asm volatile("" : "+v"(a_spec[qb]));
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    });
-
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) l_run[qb] += lsum[qb];
-    if (mask_next) {  // diagonal or ragged tile: mask, then take the row max again
-      mask_tile(s_nxt, tile_next);
+    if (wave_active) {
+      float neg_m[QB], lsum[QB], mx[QB], m_spec[QB], a_spec[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        float m = -__builtin_inff();
-        max_chunk(s_nxt, qb, 0, 16, m);
-        m_spec[qb] = new_max(m, m_run[qb]);
-        a_spec[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_spec[qb]);
+        neg_m[qb] = -m_run[qb];
+        l_run[qb] *= alpha[qb];
+        lsum[qb] = 0.0f;
+        mx[qb] = -__builtin_inff();
       }
-    }
+      const int tile_next = tile_at(j + 1);
+      const bool mask_next = needs_mask(tile_next);
+      bool any_alpha = false;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      m_run[qb] = m_spec[qb];
-      alpha[qb] = a_spec[qb];
-    }
+      for (int qb = 0; qb < QB; ++qb) any_alpha |= alpha[qb] != 1.0f;
+      const bool need_rescale = __builtin_amdgcn_ballot_w64(any_alpha) != 0;
+
+      // LDS fragment of slot b: one K read (score slots) or two transposing V reads (P.V slots).
+      bf16x8 kfr[NS_QK];
+      s16x4 vfr[C::NS_PV][2];
+      auto issue = [&](auto b_) {
+        constexpr int b = decltype(b_)::value;
+        if constexpr (b < NS_QK) {
+          kfr[b] = read_k(KR, b % KB, b / KB);
+        } else {
+          constexpr int t = (b - NS_QK) / CB, cb = (b - NS_QK) % CB;
+          vfr[b - NS_QK][0] = read_v(VR, t, cb, 0);
+          vfr[b - NS_QK][1] = read_v(VR, t, cb, 1);
+        }
+      };
+      static_for<0, PD>([&](auto b_) { issue(b_); });
+
+      static_for<0, NS>([&](auto b_) {
+        constexpr int b = decltype(b_)::value;
+        // prefetch the fragments of slot b+PD (the compiler waits for slot b's before its MFMA)
+        if constexpr (b + PD < NS) issue(std::integral_constant<int, b + PD>{});
+        if constexpr (b < NS_QK) {
+          constexpr int s = b / KB, kb = b % KB;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            s_nxt[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                kfr[b], qf[qb][s], s == 0 ? f32x16{} : s_nxt[kb][qb], 0, 0, 0);
+        } else {
+          constexpr int t = (b - NS_QK) / CB, cb = (b - NS_QK) % CB;
+          pv_mfma(cb, t, vfr[b - NS_QK][0], vfr[b - NS_QK][1]);
+        }
+        // VALU work of this slot: the exp pairs assigned to it ...
+        if constexpr (b < C::EXP_WINDOW) {
+          constexpr int p_lo = (b * C::NPAIRS + C::EXP_WINDOW - 1) / C::EXP_WINDOW;
+          constexpr int p_hi = ((b + 1) * C::NPAIRS + C::EXP_WINDOW - 1) / C::EXP_WINDOW;
+          static_for<p_lo, (p_hi < C::NPAIRS ? p_hi : C::NPAIRS)>([&](auto p_) {
+            constexpr int p = decltype(p_)::value;
+            static_assert(NS_QK + (p / 4) * CB > b, "exp pair scheduled after its P.V slot");
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) exp_pair(s_cur, qb, p, neg_m[qb], lsum[qb]);
+          });
+        }
+        // ... the pending rescale of acc, in the first slot and skipped when no row of the wave has
+        // a new max (alpha is then exactly 1 in every lane: a wave-uniform branch) ...
+        if constexpr (b == 0) {
+          if (need_rescale) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) rescale_chunk(qb, 0, 16);
+          }
+        }
+        // ... and, once the next scores are complete, a chunk of their row max, then the new max and
+        // alpha (assuming the tile needs no mask; masked tiles redo this after the slots).
+        if constexpr (b >= C::MAX_FIRST && b <= C::MAX_LAST) {
+          constexpr int nmax = C::MAX_LAST - C::MAX_FIRST + 1;
+          constexpr int r0 = (b - C::MAX_FIRST) * 16 / nmax, r1 = (b - C::MAX_FIRST + 1) * 16 / nmax;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            max_chunk(s_nxt, qb, r0, r1, mx[qb]);
+            // keep the chunk in this slot (otherwise it sinks past the edge-tile branch below)
+            asm volatile("" : "+v"(mx[qb]));
+          }
+        }
+        if constexpr (b == NS - 2) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            m_spec[qb] = new_max(mx[qb], m_run[qb]);
+            asm volatile("" : "+v"(m_spec[qb]));
+          }
+        }
+        if constexpr (b == NS - 1) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            a_spec[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_spec[qb]);
+            asm volatile("" : "+v"(a_spec[qb]));
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      });
+
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) l_run[qb] += lsum[qb];
+      if (mask_next) {  // diagonal or ragged tile: mask, then take the row max again
+        mask_tile(s_nxt, tile_next);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          float m = -__builtin_inff();
+          max_chunk(s_nxt, qb, 0, 16, m);
+          m_spec[qb] = new_max(m, m_run[qb]);
+          a_spec[qb] = __builtin_amdgcn_exp2f(m_run[qb] - m_spec[qb]);
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        m_run[qb] = m_spec[qb];
+        alpha[qb] = a_spec[qb];
+      }
+    }  // wave_active
     // the copies of the previous step (K(j+NSTAGE-1), V(j+NSTAGE-2)) have landed; this step's may
     // still be in flight. The barrier publishes them and closes every wave's reads of K(j+1), V(j).
     vmem_wait<2 * C::LOADS * (C::NSTAGE - 2)>();
@@ -635,6 +676,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
 
   // ---- last tile: softmax and P.V only.
   auto last_step = [&](int VR, f32x16 (&s_cur)[KB][QB]) {
+    if (!wave_active) return;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       float lsum = 0.0f;
@@ -682,6 +724,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   // Copies issued by the last steps may still be in flight (re-copies past the end); they must land
   // before this workgroup's LDS can be handed to another one.
   vmem_wait<0>();
+  if (!wave_active) return;  // no query row to store
 
   // ---- epilogue: O = acc / l, rounded once to bf16; LSE = ln2 * (m + log2 l).
   // Lane (n, hf) of channel block cb holds channels (D/2)*hf + 16*cb + r, r = 0..15, in order.
@@ -690,22 +733,35 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     const int row = qw0 + 32 * qb + n;
     const float l_tot = wave_sum_halves(l_run[qb]);
     float inv = 1.0f / l_tot;
-    if constexpr (C::SPARSE) inv = l_tot > 0.0f ? inv : 0.0f;  // a row that saw no key: O = 0
+    if constexpr (C::LISTED) inv = l_tot > 0.0f ? inv : 0.0f;  // a row that saw no key: O = 0
     if (row < T) {
-      char* orow = reinterpret_cast<char*>(o + head_off + (int64_t)row * D);
+      if constexpr (C::RANGE) {  // partial output of a key range: fp32
+        float* orow = reinterpret_cast<float*>(o) + head_off + (int64_t)row * D;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          u32x4 out;
+          for (int c4 = 0; c4 < 4; ++c4) {
+            f32x4 out;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            out[e] = pack_bf16x2(acc[cb][qb][8 * half + 2 * e] * inv, acc[cb][qb][8 * half + 2 * e + 1] * inv);
-          *reinterpret_cast<u32x4*>(orow + ((D / 2) * hf + 16 * cb + 8 * half) * 2) = out;
+            for (int e = 0; e < 4; ++e) out[e] = acc[cb][qb][4 * c4 + e] * inv;
+            *reinterpret_cast<f32x4*>(orow + (D / 2) * hf + 16 * cb + 4 * c4) = out;
+          }
+      } else {
+        char* orow = reinterpret_cast<char*>(o + head_off + (int64_t)row * D);
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            u32x4 out;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              out[e] = pack_bf16x2(acc[cb][qb][8 * half + 2 * e] * inv, acc[cb][qb][8 * half + 2 * e + 1] * inv);
+            *reinterpret_cast<u32x4*>(orow + ((D / 2) * hf + 16 * cb + 8 * half) * 2) = out;
+          }
         }
       }
       float lse_row = (m_run[qb] + __log2f(l_tot)) * kLn2;
-      if constexpr (C::SPARSE) lse_row = l_tot > 0.0f ? lse_row : -__builtin_inff();
+      if constexpr (C::LISTED) lse_row = l_tot > 0.0f ? lse_row : -__builtin_inff();
       if (hf == 0) lse[(int64_t)bh * T + row] = lse_row;
     }
   }

@@ -1,0 +1,78 @@
+// Log-space merge of partial attention results over disjoint key ranges (the split-KV combine).
+//
+// For a row with partial results (O_s, LSE_s) over disjoint key ranges s, the attention over the
+// union is LSE = log sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s: the logsumexp combine of
+// partial blocks in log space (ijyty.com FlashAttention article, section 2.1, the per-block lse
+// accumulation and the final division by exp(lse)). A part with LSE_s = -inf (no visible key)
+// contributes nothing; a row whose parts are all -inf gets O = 0 and LSE = -inf.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// One thread per 4 channels of a row: D/4 threads per row, 256 / (D/4) rows per workgroup. The
+// kernel is bound by HBM traffic (every part's O row is read once); the loads of several parts are
+// issued together so that their latencies overlap.
+template <int D>
+__global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__ o_parts,
+                                                       const float* __restrict__ lse_parts,
+                                                       int n_parts, __bf16* __restrict__ o,
+                                                       float* __restrict__ lse, int64_t rows) {
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  constexpr int U = 4;  // parts per batch of loads
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c4 = threadIdx.x % TPR;
+  if (row >= rows) return;
+  const float* lp = lse_parts + row;
+  const float* op = o_parts + row * D + 4 * c4;
+  const int64_t lstride = rows, ostride = rows * D;
+  // pass 1: the largest part LSE of the row
+  float m = -__builtin_inff();
+  int s = 0;
+  for (; s + 2 * U <= n_parts; s += 2 * U) {
+    float x[2 * U];
+#pragma unroll
+    for (int e = 0; e < 2 * U; ++e) x[e] = lp[(s + e) * lstride];
+#pragma unroll
+    for (int e = 0; e < 2 * U; ++e) m = fmaxf(m, x[e]);
+  }
+  for (; s < n_parts; ++s) m = fmaxf(m, lp[s * lstride]);
+  // pass 2: weights exp(LSE_s - m), their sum and the weighted sum of the parts' O
+  float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float l = 0.0f;
+  if (m > -__builtin_inff()) {
+    auto add = [&](float lse_s, float4 x) {
+      const float wgt = expf(lse_s - m);  // 0 for an empty part (LSE_s = -inf)
+      l += wgt;
+      acc[0] += wgt * x.x;
+      acc[1] += wgt * x.y;
+      acc[2] += wgt * x.z;
+      acc[3] += wgt * x.w;
+    };
+    s = 0;
+    for (; s + U <= n_parts; s += U) {
+      float ls[U];
+      float4 xs[U];
+#pragma unroll
+      for (int e = 0; e < U; ++e) {
+        ls[e] = lp[(s + e) * lstride];
+        xs[e] = *reinterpret_cast<const float4*>(op + (s + e) * ostride);
+      }
+#pragma unroll
+      for (int e = 0; e < U; ++e) add(ls[e], xs[e]);
+    }
+    for (; s < n_parts; ++s) add(lp[s * lstride], *reinterpret_cast<const float4*>(op + s * ostride));
+  }
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  bf16x4 out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[e] = (__bf16)(acc[e] * inv);  // round to nearest even
+  *reinterpret_cast<bf16x4*>(o + row * D + 4 * c4) = out;
+  if (c4 == 0) lse[row] = l > 0.0f ? m + logf(l) : -__builtin_inff();
+}
+
+}  // namespace fa

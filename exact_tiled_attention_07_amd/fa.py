@@ -57,6 +57,16 @@ def lib():
     L.fa_fwd_plan.restype = i
     L.fa_fwd_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, vp]
     L.fa_fwd_sparse.restype = i
+    L.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
+    L.fa_fwd_partial.restype = i
+    L.fa_merge.argtypes = [vp, vp, i, vp, vp, i, i, i, i, vp]
+    L.fa_merge.restype = i
+    L.fa_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
+    L.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
+    L.fa_splitkv_splits.argtypes = [i, i, i, i, i]
+    L.fa_splitkv_splits.restype = i
+    L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t, vp]
+    L.fa_fwd_splitkv.restype = i
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     L.fa_bwd.restype = i
     L.fa_strerror.argtypes = [i]
@@ -68,7 +78,7 @@ def lib():
 def header_functions():
     """Names of the functions include/fa.h declares."""
     text = open(HEADER_PATH).read()
-    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(fa_\w+)\s*\(", text, flags=re.M)))
+    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(fa_\w+)\s*\(", text, flags=re.M)))
 
 
 def strerror(status: int) -> str:
@@ -88,7 +98,9 @@ def plan(B: int, H: int, T: int, d: int, causal: bool = True, block_m: int = 0, 
     return {name: getattr(info, name) for name, _ in PlanInfo._fields_}
 
 
-def _check_inputs(q, k, v, *more):
+def _check_inputs(q, k, v, *more, keys_may_differ=False):
+    """Dtype, device, rank and contiguity of q, k, v (and of ``more``, shaped like q). With
+    ``keys_may_differ`` k and v may hold another number of keys than q has queries."""
     import torch
 
     for name, t in (("q", q), ("k", k), ("v", v), *more):
@@ -102,8 +114,10 @@ def _check_inputs(q, k, v, *more):
             raise ValueError(f"{name} must be [B, H, T, d], got {tuple(t.shape)}")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if not (q.shape == k.shape == v.shape):
-        raise ValueError(f"q, k, v shapes differ: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
+    same = (q.shape == k.shape == v.shape) if not keys_may_differ else (
+        k.shape == v.shape and q.shape[:2] == k.shape[:2] and q.shape[3] == k.shape[3])
+    if not same:
+        raise ValueError(f"q, k, v shapes do not fit: {tuple(q.shape)} {tuple(k.shape)} {tuple(v.shape)}")
     if not (q.device == k.device == v.device):
         raise ValueError("q, k, v must be on the same device")
     for name, t in more:
@@ -241,4 +255,100 @@ def fwd_sparse(q, k, v, block_mask, causal: bool = True, scale: float | None = N
         _check(lib().fa_fwd_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                    lse.data_ptr(), B, H, T, d, int(bool(causal)), scale,
                                    block_mask.data_ptr(), mh, _stream_handle(q.device, stream)))
+    return out, lse
+
+
+PARTIAL_KEY_ALIGN = 64  # FA_PARTIAL_KEY_ALIGN
+
+
+def fwd_partial(q, k, v, k_begin: int, k_end: int, causal: bool = True, scale: float | None = None,
+                o_part=None, lse_part=None, stream=None):
+    """Attention over the keys [k_begin, k_end) only (``fa_fwd_partial``): ``(o_part, lse_part)``.
+
+    q is ``[B, H, T, d]``, k and v ``[B, H, Tk, d]`` (Tk may differ from T; with the causal mask
+    the queries are the last T positions of the keys' sequence). ``o_part`` is float32
+    ``[B, H, T, d]`` (normalised over the range) and ``lse_part`` float32 ``[B, H, T]``; rows with
+    no visible key in the range get 0 and -inf. k_begin must be a multiple of 64 and k_end a
+    multiple of 64 or Tk.
+    """
+    import torch
+
+    _check_inputs(q, k, v, keys_may_differ=True)
+    B, H, T, d = q.shape
+    Tk = k.shape[2]
+    o_part = _like(q, o_part, "o_part", torch.float32)
+    lse_part = _like(q, lse_part, "lse_part", torch.float32, (B, H, T))
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        _check(lib().fa_fwd_partial(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_part.data_ptr(),
+                                    lse_part.data_ptr(), B, H, T, Tk, d, int(bool(causal)), scale,
+                                    int(k_begin), int(k_end), _stream_handle(q.device, stream)))
+    return o_part, lse_part
+
+
+def splitkv_splits(B: int, H: int, T: int, Tk: int, d: int) -> int:
+    """The split count ``fa_splitkv_splits`` suggests for this shape (enough workgroups to fill
+    the GPU, ranges of at least 512 keys)."""
+    return int(lib().fa_splitkv_splits(B, H, T, Tk, d))
+
+
+def splitkv_workspace_bytes(B: int, H: int, T: int, d: int, n_splits: int) -> int:
+    return int(lib().fa_splitkv_workspace_bytes(B, H, T, d, n_splits))
+
+
+def fwd_splitkv(q, k, v, causal: bool = True, scale: float | None = None, n_splits: int | None = None,
+                out=None, lse=None, workspace=None, stream=None):
+    """Attention with the keys split into ranges that run side by side, then merged
+    (``fa_fwd_splitkv``): returns bf16 ``o`` ``[B, H, T, d]`` and float32 ``lse``.
+
+    For few queries against many keys (T << Tk). ``n_splits`` defaults to ``splitkv_splits``;
+    ``workspace`` (a uint8 GPU tensor of at least ``splitkv_workspace_bytes`` bytes) is allocated
+    with torch when not given.
+    """
+    import torch
+
+    _check_inputs(q, k, v, keys_may_differ=True)
+    B, H, T, d = q.shape
+    Tk = k.shape[2]
+    out, lse = _outputs(q, out, lse)
+    n_splits = splitkv_splits(B, H, T, Tk, d) if n_splits is None else int(n_splits)
+    need = splitkv_workspace_bytes(B, H, T, d, n_splits) if n_splits >= 1 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if workspace.dtype != torch.uint8 or workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous uint8 tensor on q's device")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        _check(lib().fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr(), B, H, T, Tk, d, int(bool(causal)), scale, n_splits,
+                                    workspace.data_ptr(), workspace.numel(),
+                                    _stream_handle(q.device, stream)))
+    return out, lse
+
+
+def merge(o_parts, lse_parts, out=None, lse=None, stream=None):
+    """Log-space merge of partial results (``fa_merge``): returns bf16 ``o`` and float32 ``lse``.
+
+    ``o_parts`` float32 ``[n, B, H, T, d]``, ``lse_parts`` float32 ``[n, B, H, T]`` (contiguous,
+    on the GPU), e.g. stacked ``fwd_partial`` outputs over disjoint key ranges.
+    """
+    import torch
+
+    if (o_parts.dtype != torch.float32 or lse_parts.dtype != torch.float32 or o_parts.dim() != 5
+            or tuple(lse_parts.shape) != tuple(o_parts.shape[:4]) or not o_parts.is_contiguous()
+            or not lse_parts.is_contiguous() or not o_parts.is_cuda or lse_parts.device != o_parts.device):
+        raise ValueError("o_parts must be float32 [n, B, H, T, d] and lse_parts float32 [n, B, H, T], "
+                         "contiguous, on one GPU")
+    n, B, H, T, d = o_parts.shape
+    if out is None:
+        out = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=o_parts.device)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=o_parts.device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, H, T, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor [B, H, T, d]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, T]")
+    with torch.cuda.device(o_parts.device):
+        _check(lib().fa_merge(o_parts.data_ptr(), lse_parts.data_ptr(), n, out.data_ptr(),
+                              lse.data_ptr(), B, H, T, d, _stream_handle(o_parts.device, stream)))
     return out, lse

@@ -34,6 +34,8 @@
 #ifndef FA_H_
 #define FA_H_
 
+#include <stddef.h>
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -125,6 +127,64 @@ int fa_fwd_plan(int B, int H, int T, int d, int causal, int block_m, int block_n
 int fa_fwd_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                   int T, int d, int causal, float scale, const unsigned char* block_mask,
                   int mask_heads, void* stream);
+
+/*
+ * fa_fwd_partial — exact attention forward of T queries restricted to the keys [k_begin, k_end) of
+ * a sequence of Tk keys: the partial result of one key range, for a split of the keys across
+ * launches (split-KV) or devices (the keys of a sequence shard).
+ *   q        [in]  bf16 [B, H, T, d], device, 16-byte aligned
+ *   k, v     [in]  bf16 [B, H, Tk, d], device, 16-byte aligned (Tk = T for self-attention)
+ *   o_part   [out] fp32 [B, H, T, d], 16-byte aligned: softmax over the range's visible keys times V
+ *   lse_part [out] fp32 [B, H, T], 4-byte aligned: logsumexp over the range's visible keys
+ *   k_begin, k_end  0 <= k_begin <= k_end <= Tk; k_begin a multiple of FA_PARTIAL_KEY_ALIGN, k_end
+ *                   a multiple of it or Tk
+ *   causal   the queries are the last T positions of the Tk-key sequence: query i sees key j iff
+ *            j <= i + Tk - T (with Tk = T, the usual j <= i; with T > Tk, the first T - Tk queries
+ *            see no key)
+ *   other arguments as for fa_fwd (d = 64 or 128; 0 <= Tk <= FA_MAX_T)
+ * A row with no visible key in the range gets o_part = 0 and lse_part = -inf. Merging the partial
+ * results of disjoint ranges that cover [0, Tk) with fa_merge gives the full attention.
+ */
+#define FA_PARTIAL_KEY_ALIGN 64
+int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                   int B, int H, int T, int Tk, int d, int causal, float scale, int k_begin, int k_end,
+                   void* stream);
+
+/*
+ * fa_merge — combine partial results over disjoint key ranges in log space (ijyty.com
+ * FlashAttention article, section 2.1: per-block logsumexp accumulated in log space, the output
+ * divided by exp(lse) at the end):
+ *     LSE = log sum_s exp(LSE_s),   O = sum_s exp(LSE_s - LSE) O_s
+ *   o_parts   [in]  fp32 [n_parts, B, H, T, d], 16-byte aligned (e.g. fa_fwd_partial outputs)
+ *   lse_parts [in]  fp32 [n_parts, B, H, T], 4-byte aligned
+ *   n_parts         1 .. FA_MERGE_MAX_PARTS
+ *   o         [out] bf16 [B, H, T, d], 16-byte aligned; lse [out] fp32 [B, H, T], 4-byte aligned
+ *   B, H, T, d, stream as for fa_fwd. Rows whose parts are all -inf get O = 0 and LSE = -inf.
+ * Outputs must not overlap the inputs or each other. Returns FA_OK or a negative fa_status.
+ */
+#define FA_MERGE_MAX_PARTS 4096
+int fa_merge(const float* o_parts, const float* lse_parts, int n_parts, void* o, float* lse, int B,
+             int H, int T, int d, void* stream);
+
+/*
+ * fa_fwd_splitkv — exact attention of T queries over Tk keys with the keys split into equal ranges
+ * that run side by side, then merged in log space (the two steps above in one call): for shapes
+ * with few queries and many keys (T << Tk, e.g. decoding against a long prefix), where one
+ * workgroup per query block would leave most of the GPU idle.
+ *   q, k, v, causal, scale  as for fa_fwd_partial; o bf16 [B, H, T, d] and lse fp32 [B, H, T] as
+ *                           for fa_fwd
+ *   n_splits   1 .. FA_MERGE_MAX_PARTS: the keys are cut into ranges of ceil(ceil(Tk/64)/n_splits)
+ *              tiles of 64 keys; ranges past Tk are not launched
+ *   workspace  device memory of at least fa_splitkv_workspace_bytes(B, H, T, d, n_splits) bytes,
+ *              16-byte aligned, owned by the caller: the fp32 partial results (O, then LSE);
+ *              overwritten
+ * Two kernels run in order on `stream`. No allocation. Returns FA_OK or a negative fa_status.
+ */
+size_t fa_splitkv_workspace_bytes(int B, int H, int T, int d, int n_splits); /* 0 if invalid */
+int fa_splitkv_splits(int B, int H, int T, int Tk, int d); /* a split count that fills the GPU */
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int T, int Tk, int d, int causal, float scale, int n_splits, void* workspace,
+                   size_t workspace_bytes, void* stream);
 
 /*
  * fa_bwd — exact attention backward (gradients of fa_fwd), by recomputation from the saved LSE.

@@ -21,7 +21,9 @@ def call(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=1, T=8, d=64, causal=
 
 def test_library_exports_every_declared_function():
     names = fa.header_functions()
-    assert names == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_fwd_plan", "fa_fwd_sparse", "fa_strerror"]
+    assert names == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_fwd_partial", "fa_fwd_plan", "fa_fwd_sparse",
+                     "fa_fwd_splitkv", "fa_merge", "fa_splitkv_splits", "fa_splitkv_workspace_bytes",
+                     "fa_strerror"]
     lib = fa.lib()
     for n in names:
         assert hasattr(lib, n)
@@ -197,3 +199,78 @@ def test_sparse_checks():
     assert call_sparse(o=6 * A) == fa.FA_ERR_INVALID_ARG      # output over the mask
     assert call_sparse(T=0) == fa.FA_OK and call_sparse(T=0, d=128, causal=0) == fa.FA_OK
     assert fa.sparse_mask_shape(1000, 1) == (1, 8, 16) and fa.sparse_mask_shape(64, 12) == (12, 1, 1)
+
+
+# ---- fa_fwd_partial and fa_merge: checks before anything is launched
+def call_partial(B=1, H=1, T=200, Tk=None, d=64, causal=1, scale=0.125, k_begin=0, k_end=200, **kw):
+    p = dict(dict(q=A, k=2 * A, v=3 * A, o=8 * A, lse=12 * A), **kw)
+    Tk = T if Tk is None else Tk
+    return fa.lib().fa_fwd_partial(p["q"], p["k"], p["v"], p["o"], p["lse"], B, H, T, Tk, d, causal,
+                                   scale, k_begin, k_end, None)
+
+
+def test_partial_checks():
+    assert call_partial(T=0, k_end=0) == fa.FA_OK
+    assert call_partial(o=None) == fa.FA_ERR_NULL
+    assert call_partial(k_begin=32) == fa.FA_ERR_INVALID_ARG      # not on a 64-key boundary
+    assert call_partial(k_end=100) == fa.FA_ERR_INVALID_ARG       # neither aligned nor T
+    assert call_partial(k_begin=128, k_end=64) == fa.FA_ERR_INVALID_ARG
+    assert call_partial(k_end=256) == fa.FA_ERR_INVALID_ARG       # past T
+    assert call_partial(k_begin=-64) == fa.FA_ERR_INVALID_ARG
+    assert call_partial(d=32) == fa.FA_ERR_UNSUPPORTED_D
+    assert call_partial(o=8 * A + 4) == fa.FA_ERR_ALIGNMENT
+    assert call_partial(o=A) == fa.FA_ERR_INVALID_ARG             # fp32 output over q
+    assert call_partial(T=4, Tk=-1, k_end=0) == fa.FA_ERR_INVALID_ARG
+    assert call_partial(T=4, Tk=100, k_end=200) == fa.FA_ERR_INVALID_ARG  # range past Tk
+    assert call_partial(T=0, Tk=100, k_end=100) == fa.FA_OK         # no query: nothing launched
+
+
+def call_splitkv(B=1, H=2, T=4, Tk=1000, d=64, n=4, ws=16 * A, ws_bytes=None, **kw):
+    p = dict(dict(q=A, k=2 * A, v=3 * A, o=8 * A, lse=12 * A), **kw)
+    if ws_bytes is None:
+        ws_bytes = fa.lib().fa_splitkv_workspace_bytes(B, H, T, d, max(n, 1))
+    return fa.lib().fa_fwd_splitkv(p["q"], p["k"], p["v"], p["o"], p["lse"], B, H, T, Tk, d, 1, 0.125, n,
+                                   ws, ws_bytes, None)
+
+
+def test_splitkv_checks():
+    lib = fa.lib()
+    assert lib.fa_splitkv_workspace_bytes(2, 3, 5, 64, 4) == 4 * 2 * 3 * 5 * 65 * 4
+    assert lib.fa_splitkv_workspace_bytes(2, 3, 5, 64, 0) == 0
+    assert lib.fa_splitkv_workspace_bytes(-1, 3, 5, 64, 1) == 0
+    assert call_splitkv(T=0) == fa.FA_OK
+    assert call_splitkv(ws=None) == fa.FA_ERR_NULL
+    assert call_splitkv(n=0) == fa.FA_ERR_INVALID_ARG
+    assert call_splitkv(n=4097) == fa.FA_ERR_INVALID_ARG
+    assert call_splitkv(ws_bytes=100) == fa.FA_ERR_INVALID_ARG     # workspace too small
+    assert call_splitkv(d=96) == fa.FA_ERR_UNSUPPORTED_D
+    assert call_splitkv(ws=16 * A + 8) == fa.FA_ERR_ALIGNMENT
+    assert call_splitkv(o=8 * A + 2) == fa.FA_ERR_ALIGNMENT
+    assert call_splitkv(o=16 * A) == fa.FA_ERR_INVALID_ARG         # output over the workspace
+    assert call_splitkv(Tk=-5) == fa.FA_ERR_INVALID_ARG
+
+
+def test_splitkv_split_count():
+    lib = fa.lib()
+    # few query blocks against many keys: split up to 512 workgroups, 512 keys per range at least
+    assert lib.fa_splitkv_splits(1, 1, 1, 65536, 64) == 128
+    assert lib.fa_splitkv_splits(4, 12, 1, 65536, 64) == 10
+    assert lib.fa_splitkv_splits(4, 12, 4096, 4096, 64) == 1
+    assert lib.fa_splitkv_splits(1, 1, 1, 100, 64) == 1
+    assert lib.fa_splitkv_splits(0, 1, 1, 100, 64) == 1
+
+
+def call_merge(n=2, B=1, H=1, T=8, d=64, **kw):
+    p = dict(dict(op=A, lp=4 * A, o=6 * A, lse=8 * A), **kw)
+    return fa.lib().fa_merge(p["op"], p["lp"], n, p["o"], p["lse"], B, H, T, d, None)
+
+
+def test_merge_checks():
+    assert call_merge(T=0) == fa.FA_OK
+    assert call_merge(n=0) == fa.FA_ERR_INVALID_ARG
+    assert call_merge(n=4097) == fa.FA_ERR_INVALID_ARG
+    assert call_merge(op=None) == fa.FA_ERR_NULL
+    assert call_merge(d=96) == fa.FA_ERR_UNSUPPORTED_D
+    assert call_merge(o=6 * A + 8) == fa.FA_ERR_ALIGNMENT
+    assert call_merge(lse=8 * A + 2) == fa.FA_ERR_ALIGNMENT
+    assert call_merge(o=A + 1024) == fa.FA_ERR_INVALID_ARG       # over the partial outputs

@@ -1,0 +1,236 @@
+"""Parity of the split-KV path (fa_fwd_partial, fa_merge and fa_fwd_splitkv, through the C-ABI) with
+the CPU oracle.
+
+fa_fwd_partial is checked against the oracle's attention over the same key range (float32 O, so the
+dense O tolerance is a loose bound here), also with fewer (or more) queries than keys; fa_merge
+against the oracle's log-space merge on the same synthetic partial results; a partition of the
+keys, partials merged on the GPU, against the dense oracle at the dense tolerance; and the one-call
+fa_fwd_splitkv on decode-like shapes (a few queries at the end of a long key sequence) against the
+oracle of T queries over Tk keys. A one-part merge is the identity, so its O is the correctly
+rounded bf16 of the part, bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exact_tiled_attention_07_amd as fa
+from exact_tiled_attention_07_amd.inputs import WORKLOADS, make_partials, make_qkv, to_torch_bf16
+
+from parity import assert_parity, compare
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+MERGE_O_TOL = 1e-5    # fp32 weights and sums: relative error a few fp32 ulps, before the bf16 rounding
+MERGE_LSE_TOL = 1e-4   # absolute, on |LSE| up to ~20 (fp32 ulp there is 2e-6)
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def np64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check_partial(qb, kb, vb, causal, scale, k_begin, k_end, label):
+    say(f"[gpu splitkv] partial {label} shape={qb.shape} causal={causal} keys=[{k_begin},{k_end})")
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    o, lse = fa.fwd_partial(q, k, v, k_begin, k_end, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o, lse = np64(o), np64(lse)
+    o_ref, lse_ref = oracle.attention_fwd_key_range(qb, kb, vb, causal, scale, k_begin, k_end)
+    empty = np.isneginf(lse_ref)
+    np.testing.assert_array_equal(np.isneginf(lse), empty)
+    assert np.all(o[empty] == 0.0)
+    live = ~empty
+    stats = compare(o[live], lse[live], o_ref[live], lse_ref[live])
+    say(f"[gpu splitkv] partial {label} {stats} empty rows {int(empty.sum())}")
+    assert_parity(stats, label)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("T,kb_,ke_", [(1, 0, 1), (200, 0, 64), (200, 64, 200), (200, 128, 192),
+                                       (1000, 320, 704), (1000, 960, 1000), (1000, 0, 1000),
+                                       (257, 256, 256)])
+def test_partial_ranges(T, kb_, ke_, causal, d):
+    qb, kb, vb = make_qkv(1, 2, T, d, seed=4000 + T + kb_ + d)
+    check_partial(qb, kb, vb, causal, 1.0 / math.sqrt(d), kb_, ke_, f"T={T} d={d}")
+
+
+@pytest.mark.parametrize("n,T,d", [(1, 100, 64), (2, 333, 64), (4, 1000, 128), (7, 65, 64), (64, 130, 128)])
+def test_merge_against_oracle(n, T, d):
+    B, H = 2, 3
+    op, lp = make_partials(n, B, H, T, d, seed=n * 1000 + T)
+    if n > 1:
+        lp[:, 0, 0, :5] = -np.inf            # rows whose parts are all empty
+        op[:, 0, 0, :5] = 0.0
+    say(f"[gpu splitkv] merge n={n} B={B} H={H} T={T} d={d}")
+    o, lse = fa.merge(torch.from_numpy(op).to(DEV), torch.from_numpy(lp).to(DEV))
+    torch.cuda.synchronize()
+    o, lse = np64(o), np64(lse)
+    o_ref, lse_ref = oracle.merge_partials(op, lp)
+    empty = np.isneginf(lse_ref)
+    np.testing.assert_array_equal(np.isneginf(lse), empty)
+    assert np.all(o[empty] == 0.0)
+    live = ~empty
+    # O: within one bf16 rounding of the exact merge (half an ulp, plus the fp32 error before it)
+    bound = np.maximum(np.abs(o_ref[live]), 2.0 ** -126) * (2.0 ** -8) + MERGE_O_TOL * (1 + np.abs(o_ref[live]))
+    err = np.abs(o[live] - o_ref[live])
+    say(f"[gpu splitkv] merge n={n} max err O {err.max():.3e} LSE {np.abs(lse[live] - lse_ref[live]).max():.3e}")
+    assert np.all(err <= bound)
+    np.testing.assert_allclose(lse[live], lse_ref[live], rtol=0, atol=MERGE_LSE_TOL)
+
+
+def test_merge_of_one_part_is_rounding():
+    op, lp = make_partials(1, 1, 4, 300, 64, seed=9, p_empty=0.0)
+    opt, lpt = torch.from_numpy(op).to(DEV), torch.from_numpy(lp).to(DEV)
+    o, lse = fa.merge(opt, lpt)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), opt[0].to(torch.bfloat16).view(torch.int16))
+    assert torch.equal(lse, lpt[0])
+
+
+def split_and_merge(q, k, v, edges, causal, scale):
+    parts = [fa.fwd_partial(q, k, v, a, b, causal=causal, scale=scale) for a, b in zip(edges, edges[1:])]
+    op = torch.stack([p[0] for p in parts])
+    lp = torch.stack([p[1] for p in parts])
+    return fa.merge(op, lp)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("T,edges", [(200, [0, 64, 128, 200]), (1000, [0, 448, 1000]),
+                                     (1000, [0, 0, 64, 64, 512, 960, 1000]), (65, [0, 65])])
+def test_split_then_merge_is_dense(T, edges, causal, d):
+    qb, kb, vb = make_qkv(2, 2, T, d, seed=5000 + T + len(edges) + d)
+    scale = 1.0 / math.sqrt(d)
+    say(f"[gpu splitkv] split {edges} T={T} d={d} causal={causal}")
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    o, lse = split_and_merge(q, k, v, edges, causal, scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd(qb, kb, vb, causal, scale)
+    stats = compare(np64(o), np64(lse), o_ref, lse_ref)
+    say(f"[gpu splitkv] split {edges} {stats}")
+    assert_parity(stats, f"split {edges}")
+
+
+def test_split_long_sequence_sampled_rows():
+    # the T = 16384 causal workload's shape split into 4 equal key ranges; rows checked one by one
+    wl = WORKLOADS["c5a"]
+    B, H, T, d = wl.B, wl.H, wl.T, wl.d
+    qb, kb, vb = wl.make()
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    say(f"[gpu splitkv] split4 {wl.name}")
+    o, lse = split_and_merge(q, k, v, [0, 4096, 8192, 12288, 16384], True, wl.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = [(int(b), int(h), int(i)) for b, h, i in zip(rng.integers(0, B, 24), rng.integers(0, H, 24),
+                                                      rng.integers(0, T, 24))]
+    rows += [(0, 0, 0), (B - 1, H - 1, T - 1), (1, 3, 4095), (2, 5, 4096)]
+    o_ref, lse_ref = oracle.attention_rows(qb, kb, vb, True, wl.scale, [(b * H + h) * T + i for b, h, i in rows])
+    got_o = np.stack([np64(o[b, h, i]) for b, h, i in rows])
+    got_l = np.array([float(lse[b, h, i]) for b, h, i in rows])
+    stats = compare(got_o, got_l, o_ref, lse_ref)
+    say(f"[gpu splitkv] split4 {stats}")
+    assert_parity(stats, "split4 T=16384")
+
+
+def cross_inputs(B, H, T, Tk, d, seed):
+    q, _, _ = make_qkv(B, H, T, d, seed=seed)
+    _, k, v = make_qkv(B, H, Tk, d, seed=seed + 1)
+    return q, k, v
+
+
+def check_against_cross(o, lse, ref, label, sampled=None):
+    o_ref, lse_ref = ref
+    o, lse = np64(o), np64(lse)
+    if sampled is not None:
+        o, lse, o_ref, lse_ref = o[sampled], lse[sampled], o_ref[sampled], lse_ref[sampled]
+    empty = np.isneginf(lse_ref)
+    np.testing.assert_array_equal(np.isneginf(lse), empty)
+    assert np.all(o[empty] == 0.0)
+    live = ~empty
+    stats = compare(o[live], lse[live], o_ref[live], lse_ref[live])
+    say(f"[gpu splitkv] {label} {stats} empty rows {int(empty.sum())}")
+    assert_parity(stats, label)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("T,Tk,kb_,ke_,d", [(1, 1000, 0, 1000, 64), (1, 1000, 448, 960, 128),
+                                            (16, 4096, 1024, 2048, 64), (100, 40, 0, 40, 64),
+                                            (130, 515, 64, 515, 128), (200, 64, 0, 64, 64)])
+def test_partial_queries_and_keys_differ(T, Tk, kb_, ke_, d, causal):
+    qb, kb, vb = cross_inputs(1, 3, T, Tk, d, seed=6000 + T + Tk + d)
+    scale = 1.0 / math.sqrt(d)
+    say(f"[gpu splitkv] partial T={T} Tk={Tk} keys=[{kb_},{ke_}) d={d} causal={causal}")
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    o, lse = fa.fwd_partial(q, k, v, kb_, ke_, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention_fwd_cross(qb, kb, vb, causal, scale, kb_, ke_)
+    check_against_cross(o, lse, ref, f"partial T={T} Tk={Tk}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("B,H,T,Tk,d,n", [(2, 3, 1, 5000, 64, None), (2, 3, 1, 5000, 128, 7),
+                                          (1, 4, 5, 3000, 64, 1), (1, 2, 64, 3000, 64, 5),
+                                          (1, 2, 130, 2049, 128, None), (1, 2, 1, 100, 64, 50),
+                                          (2, 2, 1000, 1000, 64, 3), (1, 1, 300, 100, 64, 2)])
+def test_splitkv_against_oracle(B, H, T, Tk, d, n, causal):
+    qb, kb, vb = cross_inputs(B, H, T, Tk, d, seed=7000 + T + Tk + d)
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    used = fa.splitkv_splits(B, H, T, Tk, d) if n is None else n
+    say(f"[gpu splitkv] fwd_splitkv B={B} H={H} T={T} Tk={Tk} d={d} n_splits={used} causal={causal}")
+    o, lse = fa.fwd_splitkv(q, k, v, causal=causal, scale=scale, n_splits=n)
+    torch.cuda.synchronize()
+    check_against_cross(o, lse, oracle.attention_fwd_cross(qb, kb, vb, causal, scale), f"splitkv n={used}")
+
+
+def test_splitkv_decode_workload_sampled():
+    # decoding 16 queries against the 16384-key sequences of the B=4, H=12, d=64 workload, with the
+    # split count the library picks; every head is checked (the oracle handles 16 rows per head)
+    B, H, T, Tk, d = 4, 12, 16, 16384, 64
+    qb, kb, vb = cross_inputs(B, H, T, Tk, d, seed=71)
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    say(f"[gpu splitkv] decode B={B} H={H} T={T} Tk={Tk} n_splits={fa.splitkv_splits(B, H, T, Tk, d)}")
+    o, lse = fa.fwd_splitkv(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    check_against_cross(o, lse, oracle.attention_fwd_cross(qb, kb, vb, True, 0.125), "decode T=16 Tk=16384")
+
+
+def test_splitkv_writes_stay_inside_outputs():
+    B, H, T, Tk, d = 2, 3, 7, 1500, 64
+    qb, kb, vb = cross_inputs(B, H, T, Tk, d, seed=81)
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    n, nl, guard = B * H * T * d, B * H * T, 4096
+    big = torch.full((n + 2 * guard,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lbig = torch.full((nl + 2 * guard,), float("nan"), dtype=torch.float32, device=DEV)
+    need = fa.splitkv_workspace_bytes(B, H, T, d, 6)
+    wbig = torch.full((need + 2 * guard,), 0x5A, dtype=torch.uint8, device=DEV)
+    o, lse = big[guard:guard + n].view(B, H, T, d), lbig[guard:guard + nl].view(B, H, T)
+    fa.fwd_splitkv(q, k, v, n_splits=6, out=o, lse=lse, workspace=wbig[guard:guard + need])
+    torch.cuda.synchronize()
+    assert torch.isnan(big[:guard].float()).all() and torch.isnan(big[guard + n:].float()).all()
+    assert torch.isnan(lbig[:guard]).all() and torch.isnan(lbig[guard + nl:]).all()
+    assert (wbig[:guard] == 0x5A).all() and (wbig[guard + need:] == 0x5A).all()
+    check_against_cross(o, lse, oracle.attention_fwd_cross(qb, kb, vb, True, 0.125), "guarded")
+
+
+def test_partial_binding_rejects():
+    q = torch.zeros(1, 1, 100, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(fa.FaError):
+        fa.fwd_partial(q, q, q, 32, 100)
+    with pytest.raises(ValueError):
+        fa.merge(torch.zeros(2, 1, 1, 8, 64, device=DEV), torch.zeros(2, 1, 1, 7, device=DEV))
+    k = torch.zeros(1, 1, 300, 64, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(fa.FaError):  # range past the 300 keys
+        fa.fwd_partial(q, k, k, 0, 320)
+    with pytest.raises(ValueError):  # head dims differ
+        fa.fwd_splitkv(q, k[..., :32].contiguous(), k[..., :32].contiguous())
+    with pytest.raises(fa.FaError):
+        fa.fwd_splitkv(q, k, k, n_splits=0)
