@@ -35,14 +35,25 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
-KERNEL_SOURCES = ["exact_tiled_attention_07_amd/csrc/fa_kernel.hpp",
-                  "exact_tiled_attention_07_amd/csrc/fa_api.hip"]
+# What identifies the profiled kernel: its source and its launch plan on the profiled workload
+# (the host code around it may change without touching the kernel the counters were taken on).
+KERNEL_SOURCES = ["exact_tiled_attention_07_amd/csrc/fa_kernel.hpp"]
 BWD_FLOPS_PER_FWD = 2.5  # the usual count: the backward's matrix products are 2.5x the forward's
 BWD_SOURCES = ["exact_tiled_attention_07_amd/csrc/fa_bwd_kernel.hpp"] + KERNEL_SOURCES
+PROFILED_WORKLOAD = "c4"  # the workload of the committed counter summaries
 BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_bwd_c4_hbm_traffic.txt")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_hbm_traffic.txt")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_sq_counters.txt")
 MFMA_FLOP_PER_CLK = 256 * 4 * 1024  # dense bf16: 1024 flop per clock on each of the 1024 SIMDs
+
+
+def profiled_plan():
+    """Launch plan of the forward on the profiled workload (host logic of libfa, no GPU needed)."""
+    import exact_tiled_attention_07_amd as fa
+    from exact_tiled_attention_07_amd.inputs import WORKLOADS
+
+    w = WORKLOADS[PROFILED_WORKLOAD]
+    return fa.plan(w.B, w.H, w.T, w.d, w.causal)
 
 
 def kernel_source_hash(sources=None) -> str:
@@ -50,6 +61,7 @@ def kernel_source_hash(sources=None) -> str:
     for rel in (KERNEL_SOURCES if sources is None else sources):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    h.update(json.dumps(profiled_plan(), sort_keys=True).encode())
     return h.hexdigest()[:16]
 
 
@@ -426,7 +438,8 @@ def main(argv=None):
                     **{k2: round(v2, 5) for k2, v2 in bex.items()},
                     "roofline": {"bound": "mfma", "achieved": round(bach, 3), "peak": PEAK_BF16_TFLOPS,
                                  "unit": "TFLOP/s", "frac": round(bach / PEAK_BF16_TFLOPS, 4),
-                                 "traffic": recorded_traffic(BWD_TRAFFIC_FILE, BWD_SOURCES)},
+                                 "traffic": recorded_traffic(BWD_TRAFFIC_FILE, BWD_SOURCES)
+                                 if args.workload == PROFILED_WORKLOAD else None},
                     "kernel_source_hash": kernel_source_hash(BWD_SOURCES)}
         print(f"[bench] backward {wl.name}: {backward}", file=sys.stderr, flush=True)
         if args.only_backward:
@@ -469,8 +482,9 @@ def main(argv=None):
         base = cpu_baseline(wl)
         print(f"[bench] cpu baseline: {base}", file=sys.stderr, flush=True)
 
-    traffic = recorded_traffic()
-    clock = recorded_clock_mhz()
+    profiled = args.workload == PROFILED_WORKLOAD and tiles is None
+    traffic = recorded_traffic() if profiled else None
+    clock = recorded_clock_mhz() if profiled else None
     peak_at_clock = MFMA_FLOP_PER_CLK * clock * 1e6 / 1e12 if clock else None
     line = {
         "metric": "causal attn fwd TFLOP/s & % of bf16 MFMA peak, B4 H12 d64, T=1K..16K",
