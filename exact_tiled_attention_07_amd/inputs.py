@@ -104,3 +104,29 @@ def make_partials(n: int, B: int, H: int, T: int, d: int, seed: int, lse_sigma: 
     lse[empty] = -np.inf
     o[empty] = 0.0
     return o, lse
+
+
+def quantize_e4m3(x, descale: float):
+    """FP8 E4M3 (OCP, no infinities) codes of ``x / descale``: round to nearest even, values beyond
+    the largest finite magnitude (448) clamped to it. Returns uint8 codes."""
+    import torch
+
+    y = np.clip(np.asarray(x, dtype=np.float32) / np.float32(descale), -448.0, 448.0)
+    return torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def make_qkv_fp8(B: int, H: int, T: int, d: int, seed: int, sigma: float = 1.0):
+    """FP8 inputs: ``make_qkv``'s normal draws (same generator, same order, times sigma) quantized per
+    tensor to E4M3 with the descale factor amax / 448 (in float32), so the largest magnitude of each
+    tensor maps to the largest code. Returns ``(q8, k8, v8, (q_descale, k_descale, v_descale))``."""
+    gen = np.random.Generator(np.random.PCG64(seed))
+    codes, scales = [], []
+    for _ in range(3):  # order: q, k, v
+        x = gen.standard_normal((B, H, T, d), dtype=np.float32)
+        if sigma != 1.0:
+            x *= np.float32(sigma)
+        amax = float(np.abs(x).max()) if x.size else 1.0
+        descale = float(np.float32(max(amax, 1e-30) / 448.0))
+        codes.append(quantize_e4m3(x, descale))
+        scales.append(descale)
+    return codes[0], codes[1], codes[2], tuple(scales)

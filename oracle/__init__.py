@@ -30,9 +30,12 @@ results over disjoint key ranges (ijyty.com FlashAttention article, section 2.1)
 ``attention_fwd_cross``, the plain two-pass attention of T queries over a key range of a Tk-key
 sequence (one library matmul per head for the scores and one for P V).
 
+``attention_fwd_fp8`` decodes FP8 E4M3 codes exactly, applies the per-tensor descale factors in
+float64 and calls the float64 forward.
+
 Every function here is pinned by the ``not gpu`` tests in ``tests/test_oracle_pins.py``,
-``tests/test_oracle_bwd_pins.py``, ``tests/test_oracle_sparse_pins.py`` and
-``tests/test_oracle_splitkv_pins.py`` against closed forms, invariants, finite differences, brute
+``tests/test_oracle_bwd_pins.py``, ``tests/test_oracle_sparse_pins.py``,
+``tests/test_oracle_splitkv_pins.py`` and ``tests/test_oracle_fp8_pins.py`` against closed forms, invariants, finite differences, brute
 force and library special cases.
 """
 from __future__ import annotations
@@ -348,3 +351,40 @@ def attention_fwd_cross(q_bits, k_bits, v_bits, causal: bool, scale: float, k_be
             o[b, h] = np.where(has_key[:, None], (e @ vf) / l_safe[:, None], 0.0)
             lse[b, h] = np.where(has_key, m_safe + np.log(l_safe), -np.inf)
     return o, lse
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Decode OCP FP8 E4M3 codes (uint8) to float64, exactly.
+
+    The format (the OCP 8-bit floating point specification's E4M3, the "fn" variant with no
+    infinities): sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent 0 is subnormal
+    (m * 2^-9); S.1111.111 is NaN; the largest finite magnitude is 1.75 * 2^8 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c >> 7, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    out = sign * mag
+    return np.where((e == 15) & (m == 7), np.nan, out)
+
+
+def attention_fwd_fp8(q8, k8, v8, causal: bool, scale: float, q_descale: float, k_descale: float,
+                      v_descale: float, num_threads: int = 0):
+    """Exact attention on FP8 inputs: the inputs are the E4M3 codes times their per-tensor descale
+    factors (``q = e4m3(q8) * q_descale``, likewise k and v), and the result is the exact attention of
+    those values in float64 (``attention_fwd_f64``).
+
+    Low-precision inputs that double the matrix throughput are the pages' next step (cnblogs
+    "内核案例研究：Flash Attention", the closing section on V3: FP8 on Hopper); the decode and the
+    descale are exact in float64 (a 4-bit significand times an fp32 factor), so this is the plain
+    definition on the values the codes stand for. Returns ``(o, lse)`` float64.
+    """
+    for name, x in (("q8", q8), ("k8", k8), ("v8", v8)):
+        if np.asarray(x).dtype != np.uint8 or np.asarray(x).ndim != 4:
+            raise TypeError(f"{name}: expected FP8 E4M3 codes as uint8 [B, H, T, d]")
+    qd, kd, vd = (float(np.float32(s)) for s in (q_descale, k_descale, v_descale))
+    q = e4m3_to_f64(q8) * qd
+    k = e4m3_to_f64(k8) * kd
+    v = e4m3_to_f64(v8) * vd
+    return attention_fwd_f64(q, k, v, causal, scale, num_threads)
