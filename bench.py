@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 flop/clk x 2.4 GHz
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5033.2   # MI355X dense fp8 MFMA: twice the bf16 rate
 # What identifies the profiled kernel: its source and its launch plan on the profiled workload
 # (the host code around it may change without touching the kernel the counters were taken on).
 KERNEL_SOURCES = ["exact_tiled_attention_07_amd/csrc/fa_kernel.hpp"]
@@ -348,6 +349,37 @@ def time_splitkv(steps, warmup):
                                               "traffic": None, "algorithmic_bytes": merge_bytes}}}
 
 
+def time_fp8(names, steps, warmup):
+    """fa_fwd_fp8 on FP8 copies of the workloads (same seeds, per-tensor E4M3 quantization), against
+    the fp8 MFMA peak, with fa_fwd on the bf16 inputs of the same workload timed alongside."""
+    import torch
+
+    import exact_tiled_attention_07_amd as fa
+    from exact_tiled_attention_07_amd.inputs import WORKLOADS, make_qkv_fp8, to_torch_bf16
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for name in names:
+        wl = WORKLOADS[name]
+        few = (max(5, steps // 5), max(2, warmup // 5)) if wl.T > 4096 else (steps, warmup)
+        timed = _event_timer(stream, *few)
+        q8, k8, v8, sc = make_qkv_fp8(wl.B, wl.H, wl.T, wl.d, wl.seed, wl.sigma)
+        t8 = [torch.from_numpy(x).to(dev) for x in (q8, k8, v8)]
+        o = torch.empty((wl.B, wl.H, wl.T, wl.d), dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((wl.B, wl.H, wl.T), dtype=torch.float32, device=dev)
+        ms = timed(lambda: fa.fwd_fp8(*t8, *sc, causal=wl.causal, scale=wl.scale, out=o, lse=lse, stream=stream))
+        q, k, v = (to_torch_bf16(x, dev) for x in wl.make())
+        ms16 = timed(lambda: fa.fwd(q, k, v, causal=wl.causal, scale=wl.scale, out=o, lse=lse, stream=stream))
+        tf = wl.flops / (ms * 1e-3) / 1e12
+        out[name] = {"workload": wl.name + " (E4M3 inputs)", "ms_per_step": round(ms, 5), "tflops": round(tf, 2),
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None},
+                     "bf16_ms": round(ms16, 5), "speedup_vs_bf16": round(ms16 / ms, 3)}
+        del t8, q, k, v
+    return out
+
+
 def cpu_baseline(wl, budget_s=20.0):
     """Time the CPU oracle on a bounded sample of the workload (whole heads, all host cores)."""
     import numpy as np
@@ -406,6 +438,7 @@ def main(argv=None):
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-sparse", action="store_true")
     ap.add_argument("--no-splitkv", action="store_true")
+    ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--only-backward", action="store_true",
                     help="time fa_bwd only and print its line (for profiling the backward)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -475,6 +508,11 @@ def main(argv=None):
         splitkv = time_splitkv(args.steps, args.warmup)
         print(f"[bench] splitkv: {splitkv}", file=sys.stderr, flush=True)
 
+    fp8 = None
+    if not args.no_fp8:
+        fp8 = time_fp8(("c4", "c5a", "c5b"), args.steps, args.warmup)
+        print(f"[bench] fp8: {fp8}", file=sys.stderr, flush=True)
+
     copy_calibration(args.copy_calibration_mib)
 
     base = None
@@ -515,6 +553,7 @@ def main(argv=None):
         "backward": backward,
         "sparse": sparse,
         "splitkv": splitkv,
+        "fp8": fp8,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -8,6 +8,7 @@
 
 #include "fa.h"
 #include "fa_bwd_kernel.hpp"
+#include "fa_fp8_kernel.hpp"
 #include "fa_kernel.hpp"
 #include "fa_merge_kernel.hpp"
 
@@ -304,6 +305,47 @@ int launch_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   return launch_merge_kernel(o_parts, lse_parts, used, o, lse, rows, d, stream);
 }
 
+// FP8 forward: E4M3 inputs with per-tensor descale factors, 128 queries x 64 keys per tile.
+int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int T,
+               int d, int causal, float scale, float q_descale, float k_descale, float v_descale,
+               void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  int rc = check_sizes(B, H, T, d);
+  if (rc != FA_OK) return rc;
+  const float fs[4] = {scale, q_descale, k_descale, v_descale};
+  for (float x : fs)
+    if (!std::isfinite(x) || !(x > 0.0f)) return FA_ERR_INVALID_ARG;
+  const double sl2 = (double)scale * q_descale * k_descale * 1.4426950408889634;
+  if (!(sl2 < 3.0e38) || !(sl2 > 1.0e-37)) return FA_ERR_INVALID_ARG;  // fp32 range of the factor
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGNMENT;
+  if ((uintptr_t)lse & 3u) return FA_ERR_ALIGNMENT;
+  const size_t n_elem = (size_t)B * H * T * d;
+  const size_t in_bytes = n_elem, o_bytes = n_elem * 2, lse_bytes = (size_t)B * H * T * 4;
+  const void* ins[3] = {q, k, v};
+  for (int a = 0; a < 3; ++a)
+    if (overlaps(o, o_bytes, ins[a], in_bytes) || overlaps(lse, lse_bytes, ins[a], in_bytes))
+      return FA_ERR_INVALID_ARG;
+  if (overlaps(o, o_bytes, lse, lse_bytes)) return FA_ERR_INVALID_ARG;
+  if (n_elem == 0) return FA_OK;
+  const int nq = (T + 127) / 128;
+  const int BH = B * H;
+  const int64_t grid = (int64_t)nq * BH;
+  if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  using Fn8 = void (*)(const uint8_t*, const uint8_t*, const uint8_t*, __bf16*, float*, int, int, int,
+                       float, float);
+  Fn8 fn;
+  if (d == 64)
+    fn = causal ? &fa::fa_fwd_fp8_kernel<fa::Fp8Cfg<64, true>> : &fa::fa_fwd_fp8_kernel<fa::Fp8Cfg<64, false>>;
+  else
+    fn = causal ? &fa::fa_fwd_fp8_kernel<fa::Fp8Cfg<128, true>> : &fa::fa_fwd_fp8_kernel<fa::Fp8Cfg<128, false>>;
+  static_assert(fa::Fp8Cfg<64, true>::BM == 128 && fa::Fp8Cfg<128, true>::BM == 128, "Q block");
+  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, (const uint8_t*)q,
+                     (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse, T, nq, BH, (float)sl2,
+                     v_descale);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
 int launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int T,
                int d, int causal, float scale, void* stream) {
@@ -395,6 +437,13 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
 int fa_merge(const float* o_parts, const float* lse_parts, int n_parts, void* o, float* lse, int B,
              int H, int T, int d, void* stream) {
   return launch_merge(o_parts, lse_parts, n_parts, o, lse, B, H, T, d, stream);
+}
+
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int T,
+               int d, int causal, float scale, float q_descale, float k_descale, float v_descale,
+               void* stream) {
+  return launch_fp8(q, k, v, o, lse, B, H, T, d, causal, scale, q_descale, k_descale, v_descale,
+                    stream);
 }
 
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -67,6 +67,8 @@ def lib():
     L.fa_splitkv_splits.restype = i
     L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t, vp]
     L.fa_fwd_splitkv.restype = i
+    L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, f, f, f, vp]
+    L.fa_fwd_fp8.restype = i
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
     L.fa_bwd.restype = i
     L.fa_strerror.argtypes = [i]
@@ -181,6 +183,40 @@ def fwd_ex(q, k, v, block_m: int, block_n: int, waves: int, causal: bool = True,
         _check(lib().fa_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                lse.data_ptr(), B, H, T, d, int(bool(causal)), scale,
                                _stream_handle(q.device, stream), block_m, block_n, waves))
+    return out, lse
+
+
+def fwd_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float, causal: bool = True,
+            scale: float | None = None, out=None, lse=None, stream=None):
+    """Attention forward on FP8 E4M3 inputs (``fa_fwd_fp8``): returns bf16 ``o`` and float32 ``lse``.
+
+    ``q8``, ``k8``, ``v8``: contiguous ``[B, H, T, d]`` GPU tensors of E4M3 codes (``torch.uint8`` or
+    ``torch.float8_e4m3fn``) standing for ``code * descale`` with one descale factor per tensor.
+    ``scale`` defaults to 1/sqrt(d).
+    """
+    import torch
+
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        if not isinstance(t, torch.Tensor) or t.dtype not in (torch.uint8, torch.float8_e4m3fn):
+            raise TypeError(f"{name} must be a uint8 or float8_e4m3fn torch.Tensor")
+        if not t.is_cuda or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [B, H, T, d] GPU tensor")
+        if t.shape != q8.shape or t.device != q8.device:
+            raise ValueError("q8, k8, v8 must have one shape and one device")
+    B, H, T, d = q8.shape
+    if out is None:
+        out = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q8.device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, H, T, d) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor [B, H, T, d]")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, T]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q8.device):
+        _check(lib().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), B, H, T, d, int(bool(causal)), scale, float(q_descale),
+                                float(k_descale), float(v_descale), _stream_handle(q8.device, stream)))
     return out, lse
 
 

@@ -187,6 +187,26 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                    size_t workspace_bytes, void* stream);
 
 /*
+ * fa_fwd_fp8 — the attention forward on FP8 inputs: q, k and v are OCP FP8 E4M3 codes ("e4m3fn":
+ * bias 7, no infinities, largest magnitude 448) that stand for code * descale, one descale factor per
+ * tensor. Both matrix products run on the FP8 matrix unit (the low-precision mode that doubles matrix
+ * throughput: cnblogs "内核案例研究：Flash Attention", the closing section on its third version).
+ *   q, k, v  [in]  uint8 E4M3 codes [B, H, T, d], device, 16-byte aligned
+ *   o        [out] bf16 [B, H, T, d], device, 16-byte aligned
+ *   lse      [out] fp32 [B, H, T], device, 4-byte aligned: natural-log logsumexp of the scaled scores
+ *   scale, q_descale, k_descale, v_descale  finite and > 0: the scores are
+ *            scale * (q_descale * q) . (k_descale * k), and V is v_descale * v
+ *   B, H, T, d, causal, stream  as for fa_fwd (d = 64 or 128)
+ * Numerics: fp32 accumulation and softmax; the probabilities are rounded to E4M3 (round to nearest
+ * even, after scaling the largest weight of each row to 2^8) before the second product, which bounds
+ * the relative error of each term of O by 2^-4. O is rounded once to bf16.
+ * Returns FA_OK or a negative fa_status (checked before anything is launched).
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int T,
+               int d, int causal, float scale, float q_descale, float k_descale, float v_descale,
+               void* stream);
+
+/*
  * fa_bwd — exact attention backward (gradients of fa_fwd), by recomputation from the saved LSE.
  *
  *     dV = P^T dO,  dP = dO V^T,  D_i = dO_i . O_i,  dS = P o (dP - D),

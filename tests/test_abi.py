@@ -21,9 +21,9 @@ def call(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=1, T=8, d=64, causal=
 
 def test_library_exports_every_declared_function():
     names = fa.header_functions()
-    assert names == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_fwd_partial", "fa_fwd_plan", "fa_fwd_sparse",
-                     "fa_fwd_splitkv", "fa_merge", "fa_splitkv_splits", "fa_splitkv_workspace_bytes",
-                     "fa_strerror"]
+    assert names == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_fwd_partial", "fa_fwd_plan",
+                     "fa_fwd_sparse", "fa_fwd_splitkv", "fa_merge", "fa_splitkv_splits",
+                     "fa_splitkv_workspace_bytes", "fa_strerror"]
     lib = fa.lib()
     for n in names:
         assert hasattr(lib, n)
@@ -274,3 +274,23 @@ def test_merge_checks():
     assert call_merge(o=6 * A + 8) == fa.FA_ERR_ALIGNMENT
     assert call_merge(lse=8 * A + 2) == fa.FA_ERR_ALIGNMENT
     assert call_merge(o=A + 1024) == fa.FA_ERR_INVALID_ARG       # over the partial outputs
+
+
+def call_fp8(B=1, H=1, T=200, d=64, causal=1, scale=0.125, qd=0.01, kd=0.01, vd=0.01, **kw):
+    p = dict(dict(q=A, k=2 * A, v=3 * A, o=8 * A, lse=12 * A), **kw)
+    return fa.lib().fa_fwd_fp8(p["q"], p["k"], p["v"], p["o"], p["lse"], B, H, T, d, causal, scale,
+                               qd, kd, vd, None)
+
+
+def test_fp8_checks():
+    assert call_fp8(T=0) == fa.FA_OK
+    assert call_fp8(v=None) == fa.FA_ERR_NULL
+    assert call_fp8(d=96) == fa.FA_ERR_UNSUPPORTED_D
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert call_fp8(qd=bad) == fa.FA_ERR_INVALID_ARG
+        assert call_fp8(vd=bad) == fa.FA_ERR_INVALID_ARG
+        assert call_fp8(scale=bad) == fa.FA_ERR_INVALID_ARG
+    assert call_fp8(qd=1e-30, kd=1e-30) == fa.FA_ERR_INVALID_ARG   # score factor underflows fp32
+    assert call_fp8(k=2 * A + 8) == fa.FA_ERR_ALIGNMENT
+    assert call_fp8(lse=12 * A + 2) == fa.FA_ERR_ALIGNMENT
+    assert call_fp8(o=A + 64) == fa.FA_ERR_INVALID_ARG             # output over q

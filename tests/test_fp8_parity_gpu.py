@@ -1,0 +1,202 @@
+"""Parity of the FP8 forward (fa_fwd_fp8, through the C-ABI) with the CPU oracle on the same FP8
+codes (exact attention of the dequantized values in float64).
+
+Tolerance, derived from the arithmetic. The kernel's one added rounding is that of the weights
+p'_j = 2^8 exp(s_j - m) to E4M3 before the second product: a relative error of at most 2^-4 for
+p'_j >= 2^-6 and an absolute error of at most 2^-10 below (the subnormal spacing is 2^-9). With
+l' = sum p'_j = 2^8 L and W_c = sum_j p_j |v_jc| (p normalised), each output element obeys
+
+    |O_gpu - O| <= 2^-4 W_c + 2^-18 sum_j |v_jc| / L + 2^-9 |O| + 1e-3 W_c + 1e-6,
+
+where 2^-9 |O| is the final bf16 rounding and 1e-3 W_c covers fp32 accumulation over up to 16384
+terms (n u = 16384 x 6e-8) and the fp32 score factor.
+
+The FP8 MFMA does not accumulate its 64 products exactly in fp32: measured on the device over 20,480
+outputs of random full-range E4M3 operands, its result differs from the exact dot product by at most
+1.8e-4 x sum_k |a_k b_k| (2.6e-5 for quantized normal data). The tests take EPS_MFMA = 2^-12 = 2.4e-4
+for that. A score s_j = scale q_i . k_j then carries an error of at most
+dS_i = EPS_MFMA * scale * q_descale * k_descale * max_j sum_c |q8_ic k8_jc|, which moves LSE by at
+most dS_i (logsumexp is 1-Lipschitz in the max norm) and each weight p_j by a factor within
+exp(+-2 dS_i); the product P.V adds EPS_MFMA W_c. So the element bound gains (2 dS_i + EPS_MFMA) W_c
+and LSE is checked against dS_i + 1e-5 + 1e-6 |LSE|. The bounds are checked element by element.
+It is loose because rounding errors cancel, so the mean square error is also checked against its
+expectation: RNE to 3 mantissa bits has E[rel^2] = 2^-8 / 6 (relative error uniform within half an
+ulp, mantissa fraction uniform), so E[(O_gpu - O)_c^2] = 2^-8 / 6 sum_j p_j^2 v_jc^2 (+ the bf16
+term); the measured mean over all elements must stay below 3 times the predicted mean. LSE uses the
+fp32 weights (not the rounded ones): its error is that of the scores.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exact_tiled_attention_07_amd as fa
+from exact_tiled_attention_07_amd.inputs import WORKLOADS, make_qkv_fp8
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+EPS_MFMA = 2.0 ** -12  # FP8 MFMA accumulation error per unit of sum |a_k b_k| (measured 1.8e-4 at most)
+MSE_FACTOR = 3.0
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def error_model(q8, k8, v8, scales, causal, scale, heads_rows):
+    """Per selected row: the element bound on O, the bound on LSE and the predicted squared error of O
+    (numpy float64). heads_rows: list of (b, h, i)."""
+    qd, kd, vd = (float(np.float32(s)) for s in scales)
+    bounds, lbounds, pred = [], [], []
+    cache = {}
+    for b, h, i in heads_rows:
+        if (b, h) not in cache:
+            cache[(b, h)] = (oracle.e4m3_to_f64(q8[b, h]) * qd, oracle.e4m3_to_f64(k8[b, h]) * kd,
+                             oracle.e4m3_to_f64(v8[b, h]) * vd)
+        qf, kf, vf = cache[(b, h)]
+        keys = i + 1 if causal else kf.shape[0]
+        s = scale * (kf[:keys] @ qf[i])
+        ds = EPS_MFMA * scale * float((np.abs(kf[:keys]) @ np.abs(qf[i])).max())
+        e = np.exp(s - s.max())
+        L = e.sum()
+        p = e / L
+        av = np.abs(vf[:keys])
+        W = p @ av
+        o = p @ vf[:keys]
+        lse = s.max() + np.log(L)
+        bounds.append(2.0 ** -4 * W + 2.0 ** -18 * av.sum(axis=0) / L + 2.0 ** -9 * np.abs(o)
+                      + (1e-3 + EPS_MFMA + 2 * ds) * W + 1e-6)
+        lbounds.append(ds + 1e-5 + 1e-6 * abs(lse))
+        pred.append(2.0 ** -8 / 6 * ((p ** 2) @ (vf[:keys] ** 2)) + (2.0 ** -9 * o) ** 2 / 3)
+    return np.array(bounds), np.array(lbounds), np.array(pred)
+
+
+def run_gpu(q8, k8, v8, scales, causal, scale):
+    t = [torch.from_numpy(x).to(DEV) for x in (q8, k8, v8)]
+    o, lse = fa.fwd_fp8(*t, *scales, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def check(q8, k8, v8, scales, causal, scale, label, rows=None):
+    B, H, T, d = q8.shape
+    say(f"[gpu fp8] {label} shape={q8.shape} causal={causal} scale={scale}")
+    o, lse = run_gpu(q8, k8, v8, scales, causal, scale)
+    if rows is None:
+        o_ref, lse_ref = oracle.attention_fwd_fp8(q8, k8, v8, causal, scale, *scales)
+        rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(T)]
+        o_ref = o_ref.reshape(-1, d)
+        lse_ref = lse_ref.reshape(-1)
+    else:
+        # oracle on whole heads only where needed: the rows' heads, by the row-wise numpy model below
+        o_ref = None
+    bound, lbound, pred = error_model(q8, k8, v8, scales, causal, scale, rows)
+    got_o = np.stack([o[b, h, i] for b, h, i in rows])
+    got_l = np.array([lse[b, h, i] for b, h, i in rows])
+    if o_ref is None:
+        sub = {}
+        for b, h, i in rows:
+            sub.setdefault((b, h), []).append(i)
+        ref_o, ref_l = [], []
+        for (b, h), idx in sub.items():
+            oo, ll = oracle.attention_fwd_fp8(q8[b:b + 1, h:h + 1], k8[b:b + 1, h:h + 1], v8[b:b + 1, h:h + 1],
+                                              causal, scale, *scales)
+            for i in idx:
+                ref_o.append(oo[0, 0, i]); ref_l.append(ll[0, 0, i])
+        order = [(b, h, i) for (b, h), idx in sub.items() for i in idx]
+        pos = {r: n for n, r in enumerate(order)}
+        o_ref = np.stack([ref_o[pos[r]] for r in rows])
+        lse_ref = np.array([ref_l[pos[r]] for r in rows])
+    err = np.abs(got_o - o_ref)
+    lerr = np.abs(got_l - lse_ref)
+    mse, pmse = float((err ** 2).mean()), float(pred.mean())
+    say(f"[gpu fp8] {label} max|dO| {err.max():.3e} max ratio to bound {(err / bound).max():.3f} "
+        f"mse {mse:.3e} predicted {pmse:.3e} max|dLSE| {lerr.max():.2e} (ratio {(lerr / lbound).max():.3f})")
+    assert np.isfinite(got_o).all() and np.isfinite(got_l).all()
+    assert np.all(err <= bound), f"{label}: element bound exceeded"
+    assert mse <= MSE_FACTOR * pmse, f"{label}: mse {mse} vs predicted {pmse}"
+    assert np.all(lerr <= lbound), f"{label}: lse {lerr.max()}"
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 129, 255, 1000])
+def test_fp8_ragged_and_tiny_lengths(T, causal, d):
+    q8, k8, v8, scales = make_qkv_fp8(1, 2, T, d, seed=8000 + T + d)
+    check(q8, k8, v8, scales, causal, 1.0 / math.sqrt(d), f"T={T} d={d}")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_fp8_configs(name):
+    wl = WORKLOADS[name]
+    q8, k8, v8, scales = make_qkv_fp8(wl.B, wl.H, wl.T, wl.d, wl.seed, wl.sigma)
+    check(q8, k8, v8, scales, wl.causal, wl.scale, wl.name + " fp8")
+
+
+@pytest.mark.parametrize("name", ["c4", "c5a", "c5b"])
+def test_fp8_full_size_sampled_rows(name):
+    wl = WORKLOADS[name]
+    q8, k8, v8, scales = make_qkv_fp8(wl.B, wl.H, wl.T, wl.d, wl.seed, wl.sigma)
+    rng = np.random.default_rng(17)
+    rows = [(int(b), int(h), int(i)) for b, h, i in zip(rng.integers(0, wl.B, 40), rng.integers(0, wl.H, 40),
+                                                      rng.integers(0, wl.T, 40))]
+    rows += [(0, 0, 0), (0, 0, 63), (0, 0, 64), (wl.B - 1, wl.H - 1, wl.T - 1), (1, 2, 4095)]
+    rows = sorted(set(rows))
+    # the oracle runs on whole heads; keep the number of distinct heads small
+    heads = sorted({(b, h) for b, h, _ in rows})[:6]
+    rows = [r for r in rows if (r[0], r[1]) in heads]
+    check(q8, k8, v8, scales, wl.causal, wl.scale, wl.name + " fp8 sampled", rows=rows)
+
+
+def test_fp8_scales_and_descales():
+    q8, k8, v8, scales = make_qkv_fp8(2, 2, 300, 64, seed=81)
+    check(q8, k8, v8, scales, True, 0.01, "scale 0.01")
+    check(q8, k8, v8, scales, False, 1.0, "scale 1")
+    check(q8, k8, v8, (scales[0] * 4, scales[1] * 3, scales[2] * 0.5), True, 0.125, "descales x4 x3 x0.5")
+
+
+def test_fp8_closed_forms():
+    T = 200
+    q8, k8, v8, scales = make_qkv_fp8(1, 2, T, 64, seed=83)
+    # causal row 0 sees key 0 only: O[0] = v_descale * e4m3(V[0]) rounded to bf16, exactly
+    o, lse = run_gpu(q8, k8, v8, scales, True, 0.125)
+    v0 = oracle.e4m3_to_f64(v8[:, :, 0]) * float(np.float32(scales[2]))
+    ref = torch.from_numpy(v0.astype(np.float32)).to(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(o[:, :, 0], ref)
+    # Q = 0: every weight equal; causal row i is the mean of V[0..i]
+    qz = np.zeros_like(q8)
+    o, lse = run_gpu(qz, k8, v8, scales, True, 0.125)
+    vf = oracle.e4m3_to_f64(v8) * float(np.float32(scales[2]))
+    mean = np.cumsum(vf, axis=2) / np.arange(1, T + 1)[None, None, :, None]
+    np.testing.assert_allclose(o, mean, rtol=2.0 ** -8, atol=1e-6)
+    np.testing.assert_allclose(lse, np.log(np.arange(1, T + 1))[None, None, :] * np.ones((1, 2, 1)), atol=1e-5)
+
+
+def test_fp8_writes_stay_inside_outputs_and_are_deterministic():
+    B, H, T, d = 2, 3, 333, 64
+    q8, k8, v8, scales = make_qkv_fp8(B, H, T, d, seed=85)
+    t = [torch.from_numpy(x).to(DEV) for x in (q8, k8, v8)]
+    n, nl, guard = B * H * T * d, B * H * T, 4096
+    big = torch.full((n + 2 * guard,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lbig = torch.full((nl + 2 * guard,), float("nan"), dtype=torch.float32, device=DEV)
+    o, lse = big[guard:guard + n].view(B, H, T, d), lbig[guard:guard + nl].view(B, H, T)
+    fa.fwd_fp8(*t, *scales, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isnan(big[:guard].float()).all() and torch.isnan(big[guard + n:].float()).all()
+    assert torch.isnan(lbig[:guard]).all() and torch.isnan(lbig[guard + nl:]).all()
+    o2, l2 = fa.fwd_fp8(*[x.view(torch.float8_e4m3fn) for x in t], *scales)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
+
+
+def test_fp8_binding_rejects():
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.uint8, device=DEV)
+    with pytest.raises(TypeError):
+        fa.fwd_fp8(q.to(torch.int8), q, q, 1.0, 1.0, 1.0)
+    with pytest.raises(fa.FaError):
+        fa.fwd_fp8(q, q, q, 0.0, 1.0, 1.0)
+    with pytest.raises(ValueError):
+        fa.fwd_fp8(q, q[:, :, :4].contiguous(), q, 1.0, 1.0, 1.0)
