@@ -44,6 +44,10 @@ BWD_SOURCES = ["exact_tiled_attention_07_amd/csrc/fa_bwd_kernel.hpp"] + KERNEL_S
 PROFILED_WORKLOAD = "c4"  # the workload of the committed counter summaries
 BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_bwd_c4_hbm_traffic.txt")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_hbm_traffic.txt")
+FP8_SOURCES = ["exact_tiled_attention_07_amd/csrc/fa_fp8_kernel.hpp"] + KERNEL_SOURCES
+FP8_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_fp8_c4_hbm_traffic.txt")
+SPLITKV_SOURCES = KERNEL_SOURCES + ["exact_tiled_attention_07_amd/csrc/fa_merge_kernel.hpp"]
+SPLITKV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_splitkv_hbm_traffic.txt")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_c4_sq_counters.txt")
 MFMA_FLOP_PER_CLK = 256 * 4 * 1024  # dense bf16: 1024 flop per clock on each of the 1024 SIMDs
 
@@ -66,14 +70,15 @@ def kernel_source_hash(sources=None) -> str:
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(path=None, sources=None):
-    """HBM bytes per launch from a committed counter summary, if taken on these sources."""
+def recorded_traffic(path=None, sources=None, key="hbm_bytes_per_launch"):
+    """HBM bytes per launch (or per call, under another key) from a committed counter summary, if
+    taken on these sources."""
     path = TRAFFIC_FILE if path is None else path
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_hash = re.search(r"kernel_source_hash:\s*(\w+)", text)
-    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    m_bytes = re.search(re.escape(key) + r":\s*([0-9.eE+]+)", text)
     if not m_hash or not m_bytes or m_hash.group(1) != kernel_source_hash(sources):
         return None
     return float(m_bytes.group(1))
@@ -310,12 +315,15 @@ def time_splitkv(steps, warmup):
         # round trip through the workspace is the split's own cost, so it is not counted)
         alg = B * H * (2 * T * d * 2 + 2 * Tk * d * 2 + T * 4)
         gbs = alg / (ms * 1e-3) / 1e9
-        decode.append({"shape": f"B{B} H{H} T{T} Tk{Tk} d{d} causal", "n_splits": n,
+        shape = f"B{B} H{H} T{T} Tk{Tk} d{d} causal"
+        decode.append({"shape": shape, "n_splits": n,
                        "ms_per_step": round(ms, 5), "no_split_ms": round(ms1, 5),
                        "speedup_vs_no_split": round(ms1 / ms, 3),
                        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                                    "traffic": None, "algorithmic_bytes": alg}})
+                                    "traffic": recorded_traffic(SPLITKV_TRAFFIC_FILE, SPLITKV_SOURCES,
+                                                                f"hbm_bytes_per_call[{shape}]"),
+                                    "algorithmic_bytes": alg}})
         del ws
     wl = WORKLOADS["c5a"]
     q, k, v = (to_torch_bf16(x, dev) for x in wl.make())
@@ -346,7 +354,10 @@ def time_splitkv(steps, warmup):
                            "overhead_vs_dense": round(ms_sh / ms_dense, 3), "merge_ms": round(ms_merge, 5),
                            "merge_roofline": {"bound": "hbm", "achieved": round(mgbs, 1), "peak": PEAK_HBM_GBS,
                                               "unit": "GB/s", "frac": round(mgbs / PEAK_HBM_GBS, 4),
-                                              "traffic": None, "algorithmic_bytes": merge_bytes}}}
+                                              "traffic": recorded_traffic(
+                                                  SPLITKV_TRAFFIC_FILE, SPLITKV_SOURCES,
+                                                  f"hbm_bytes_per_merge[{wl.name} x{shards}]"),
+                                              "algorithmic_bytes": merge_bytes}}}
 
 
 def time_fp8(names, steps, warmup):
@@ -374,7 +385,9 @@ def time_fp8(names, steps, warmup):
         tf = wl.flops / (ms * 1e-3) / 1e12
         out[name] = {"workload": wl.name + " (E4M3 inputs)", "ms_per_step": round(ms, 5), "tflops": round(tf, 2),
                      "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_FP8_TFLOPS,
-                                  "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4), "traffic": None},
+                                  "unit": "TFLOP/s", "frac": round(tf / PEAK_FP8_TFLOPS, 4),
+                                  "traffic": recorded_traffic(FP8_TRAFFIC_FILE, FP8_SOURCES) if name == PROFILED_WORKLOAD
+                                  else None},
                      "bf16_ms": round(ms16, 5), "speedup_vs_bf16": round(ms16 / ms, 3)}
         del t8, q, k, v
     return out

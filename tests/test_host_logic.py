@@ -35,6 +35,23 @@ def test_bench_backward_traffic_record_matches_sources():
         assert t is None
 
 
+@pytest.mark.parametrize("path,sources,key", [
+    (bench.FP8_TRAFFIC_FILE, bench.FP8_SOURCES, "hbm_bytes_per_launch"),
+    (bench.SPLITKV_TRAFFIC_FILE, bench.SPLITKV_SOURCES, "hbm_bytes_per_call[B4 H12 T1 Tk16384 d64 causal]"),
+    (bench.SPLITKV_TRAFFIC_FILE, bench.SPLITKV_SOURCES, "hbm_bytes_per_call[B4 H12 T16 Tk16384 d64 causal]"),
+    (bench.SPLITKV_TRAFFIC_FILE, bench.SPLITKV_SOURCES, "hbm_bytes_per_merge[c5a_causal_B4_H12_T16384_d64 x4]"),
+])
+def test_bench_other_traffic_records_match_sources(path, sources, key):
+    os_ = __import__("os")
+    text = open(path).read() if os_.path.exists(path) else ""
+    t = bench.recorded_traffic(path, sources, key)
+    if bench.kernel_source_hash(sources) in text and key in text:
+        assert t is not None and t > 0
+    else:
+        assert t is None
+    assert bench.recorded_traffic(path, sources, key + "x") is None  # an unknown key reads nothing
+
+
 def test_bench_clock_record_matches_sources():
     c = bench.recorded_clock_mhz()
     text = open(bench.COUNTERS_FILE).read() if __import__("os").path.exists(bench.COUNTERS_FILE) else ""
