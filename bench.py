@@ -487,6 +487,15 @@ def main(argv=None):
                                  "traffic": recorded_traffic(BWD_TRAFFIC_FILE, BWD_SOURCES)
                                  if args.workload == PROFILED_WORKLOAD else None},
                     "kernel_source_hash": kernel_source_hash(BWD_SOURCES)}
+        # the d = 128 backward on the non-causal d = 128 workload (fewer steps: ~5.5 TFLOP per call)
+        w128 = WORKLOADS["c5b"]
+        ms128, ex128 = time_backward(w128, max(5, args.steps // 20), max(2, args.warmup // 20))
+        tf128 = BWD_FLOPS_PER_FWD * w128.flops / (ms128 * 1e-3) / 1e12
+        backward["d128"] = {"workload": w128.name, "ms_per_step": round(ms128, 5), "tflops": round(tf128, 3),
+                            "median_ms": round(ex128["median_ms"], 5),
+                            "roofline": {"bound": "mfma", "achieved": round(tf128, 3), "peak": PEAK_BF16_TFLOPS,
+                                         "unit": "TFLOP/s", "frac": round(tf128 / PEAK_BF16_TFLOPS, 4),
+                                         "traffic": None}}
         print(f"[bench] backward {wl.name}: {backward}", file=sys.stderr, flush=True)
         if args.only_backward:
             copy_calibration(args.copy_calibration_mib)

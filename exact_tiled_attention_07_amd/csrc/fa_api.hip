@@ -346,13 +346,17 @@ int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   return FA_OK;
 }
 
+template <int D>
+int launch_bwd_kernels(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H,
+                       int T, int causal, float scale, void* stream);
+
 int launch_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H, int T,
                int d, int causal, float scale, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
   int rc = check_sizes(B, H, T, d);
   if (rc != FA_OK) return rc;
-  if (d != 64) return FA_ERR_UNSUPPORTED_D;
   if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
        (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u)
@@ -372,8 +376,19 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* o, const
   }
   if (n_elem == 0) return FA_OK;
 
-  using Cc = fa::BwdCfg<64, true>;
-  using Cf = fa::BwdCfg<64, false>;
+  return d == 64 ? launch_bwd_kernels<64>(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, T, causal,
+                                           scale, stream)
+                 : launch_bwd_kernels<128>(q, k, v, o, lse, dout, dq, dk, dv, delta, B, H, T, causal,
+                                           scale, stream);
+}
+
+// The two backward kernels for head dim D: dQ and D first, then dK and dV (which read D).
+template <int D>
+int launch_bwd_kernels(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, float* delta, int B, int H,
+                       int T, int causal, float scale, void* stream) {
+  using Cc = fa::BwdCfg<D, true>;
+  using Cf = fa::BwdCfg<D, false>;
   const int nb = (T + Cc::BM - 1) / Cc::BM;  // query blocks (dQ kernel) = key blocks (dK/dV kernel)
   const int BH = B * H;
   const int64_t grid = (int64_t)nb * BH;

@@ -1,4 +1,4 @@
-// Exact attention backward for gfx950 (CDNA4), d = 64: dQ, dK and dV of O = softmax(scale Q K^T) V
+// Exact attention backward for gfx950 (CDNA4), d = 64 and 128: dQ, dK and dV of O = softmax(scale Q K^T) V
 // from the saved per-row logsumexp, by recomputing the probabilities block by block.
 //
 // Method (what is computed and in which order):
@@ -45,7 +45,7 @@ struct BwdCfg {
   static constexpr int PT = BN / 16;                 // k-steps over a streamed tile's rows
   static constexpr int STATS_BYTES = 2 * BN * 4;     // LSE and D of a Q tile (dK/dV kernel)
   static constexpr int LDS_BYTES = 4 * TILE_BYTES + 2 * STATS_BYTES;
-  static_assert(D == 64, "backward: head dim 64");
+  static_assert(D == 64 || D == 128, "backward: head dim");
   static_assert(LOADS >= 1 && LOADS * 16 * THREADS == TILE_BYTES, "tile load split");
 };
 

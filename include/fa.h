@@ -225,7 +225,7 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
  *                  the second kernel; its content after the call is that value)
  *   B, H, T, causal, scale, stream: as for fa_fwd (o and lse must come from fa_fwd with the same
  *   q, k, causal and scale)
- *   d        head dimension: 64 (d = 128 returns FA_ERR_UNSUPPORTED_D)
+ *   d        head dimension: 64 or 128
  * The outputs dq, dk, dv and delta must not overlap each other or any input. Two kernels run in
  * order on `stream` (dQ and D, then dK and dV); no atomics, no allocation.
  * Returns FA_OK or a negative fa_status (checked before anything is launched).

@@ -151,7 +151,7 @@ def test_bwd_null_pointers():
 def test_bwd_sizes_head_dim_scale():
     assert call_bwd(T=-1) == fa.FA_ERR_INVALID_ARG
     assert call_bwd(B=1 << 13, H=1 << 12) == fa.FA_ERR_INVALID_ARG
-    assert call_bwd(d=128) == fa.FA_ERR_UNSUPPORTED_D  # the backward is d = 64 only
+    assert call_bwd(d=96) == fa.FA_ERR_UNSUPPORTED_D  # the backward takes d = 64 or 128
     assert call_bwd(d=32) == fa.FA_ERR_UNSUPPORTED_D
     for sc in (0.0, -1.0, float("nan"), float("inf")):
         assert call_bwd(scale=sc) == fa.FA_ERR_INVALID_ARG

@@ -8,6 +8,11 @@ those roundings, on the inputs of this file, reaches an element error of 0.108 (
 head) in dQ for the sigma-4 scores (the dominant weight's dS is a small difference of two large
 terms, and the rounding of O enters through D) and an RMS error of 0.59% of the RMS. The bounds
 below are about twice that: 0.2 (|ref| + rms) per element and 1.5% RMS.
+
+Where a gradient is exactly zero by cancellation (one visible key: dS = P (dP - D) with dP = D), the
+relative bounds say nothing, so both checks also admit an absolute floor: dP and D are fp32 sums of
+d products, each off by at most d 2^-24 sum_c |dO_c| max|v|, and the rows of P sum to one, so
+dQ = scale dS K (dK = scale dS^T Q) is off by at most 2 scale d 2^-24 max|k| (max|q|) times that.
 """
 import math
 
@@ -30,11 +35,12 @@ def say(msg):
     print(msg, flush=True)
 
 
-def grad_tolerance(name, gpu, ref):
-    """Element and RMS check of one gradient tensor [B, H, T, d] (or delta [B, H, T])."""
+def grad_tolerance(name, gpu, ref, atol=0.0):
+    """Element and RMS check of one gradient tensor [B, H, T, d] (or delta [B, H, T]); atol is the
+    absolute floor of the fp32 cancellation in dS (see the module docstring)."""
     axes = tuple(range(2, ref.ndim))
     rms_head = np.sqrt((ref ** 2).mean(axis=axes, keepdims=True))
-    err = np.abs(gpu - ref)
+    err = np.maximum(np.abs(gpu - ref) - atol, 0.0)
     ratio = err / (np.abs(ref) + rms_head + 1e-30)
     rms_ratio = math.sqrt(float((err ** 2).mean()) / max(float((ref ** 2).mean()), 1e-300))
     stats = {"max_err": float(err.max()) if err.size else 0.0,
@@ -58,15 +64,20 @@ def check(qb, kb, vb, dob, causal, scale, label):
     say(f"[gpu bwd] {label} shape={qb.shape} causal={causal} scale={scale}")
     got = run_gpu(qb, kb, vb, dob, causal, scale)
     ref = oracle.attention_bwd(qb, kb, vb, dob, causal, scale)
-    stats = {n: grad_tolerance(n, g, r) for n, g, r in zip(("dq", "dk", "dv", "delta"), got, ref)}
+    q, k, v, do = (np.abs(bf16_bits_to_f32(x).astype(np.float64)) for x in (qb, kb, vb, dob))
+    d = q.shape[-1]
+    cancel = d * 2.0 ** -24 * float(do.sum(axis=-1).max(initial=0.0)) * float(v.max(initial=0.0))
+    floors = (2 * scale * float(k.max(initial=0.0)) * cancel, 2 * scale * float(q.max(initial=0.0)) * cancel,
+              0.0, 0.0)
+    stats = {n: grad_tolerance(n, g, r, a) for n, g, r, a in zip(("dq", "dk", "dv", "delta"), got, ref, floors)}
     say(f"[gpu bwd] {label} " + " ".join(f"{n}: {s['max_ratio']:.4f}/{s['rms_ratio']:.4f}"
                                          for n, s in stats.items()))
     return got, ref
 
 
-def inputs(B, H, T, seed, sigma=1.0):
-    qb, kb, vb = make_qkv(B, H, T, 64, seed=seed, sigma=sigma)
-    dob, _, _ = make_qkv(B, H, T, 64, seed=seed + 7919)
+def inputs(B, H, T, seed, sigma=1.0, d=64):
+    qb, kb, vb = make_qkv(B, H, T, d, seed=seed, sigma=sigma)
+    dob, _, _ = make_qkv(B, H, T, d, seed=seed + 7919)
     return qb, kb, vb, dob
 
 
@@ -74,6 +85,18 @@ def inputs(B, H, T, seed, sigma=1.0):
 @pytest.mark.parametrize("T", [1, 2, 31, 63, 64, 65, 127, 128, 129, 255, 257, 1000])
 def test_bwd_ragged_and_tiny_lengths(T, causal):
     check(*inputs(1, 3, T, 2000 + T), causal, 0.125, f"T={T}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("T", [1, 2, 63, 65, 128, 129, 257, 1000])
+def test_bwd_head_dim_128(T, causal):
+    check(*inputs(1, 3, T, 3000 + T, d=128), causal, 1.0 / math.sqrt(128), f"d=128 T={T}")
+
+
+def test_bwd_head_dim_128_long_and_wide_scores():
+    # two heads of the non-causal d = 128 workload's shape at T = 2048, then sigma-2 causal inputs
+    check(*inputs(1, 2, 2048, 6, d=128), False, 1.0 / math.sqrt(128), "d=128 T=2048 non-causal")
+    check(*inputs(1, 2, 1500, 7, sigma=2.0, d=128), True, 1.0 / math.sqrt(128), "d=128 T=1500 sigma2")
 
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c3"])
@@ -117,9 +140,10 @@ def test_bwd_closed_forms():
     assert np.abs(got[0]).max() < 0.02 and np.abs(got[1]).max() < 0.02, (np.abs(got[0]).max(), np.abs(got[1]).max())
 
 
-def test_bwd_writes_stay_inside_outputs_and_are_deterministic():
-    B, H, T, d = 2, 3, 333, 64
-    qb, kb, vb, dob = inputs(B, H, T, 41)
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_writes_stay_inside_outputs_and_are_deterministic(d):
+    B, H, T = 2, 3, 333
+    qb, kb, vb, dob = inputs(B, H, T, 41, d=d)
     q, k, v, do = (to_torch_bf16(x, DEV) for x in (qb, kb, vb, dob))
     o, lse = fa.fwd(q, k, v, causal=True)
     n, nl, guard = B * H * T * d, B * H * T, 4096
@@ -142,9 +166,9 @@ def test_bwd_writes_stay_inside_outputs_and_are_deterministic():
 
 
 def test_bwd_binding_rejects():
-    q = torch.zeros(1, 1, 8, 128, dtype=torch.bfloat16, device=DEV)
+    q = torch.zeros(1, 1, 8, 96, dtype=torch.bfloat16, device=DEV)
     lse = torch.zeros(1, 1, 8, dtype=torch.float32, device=DEV)
-    with pytest.raises(fa.FaError):  # the backward supports d = 64 only
+    with pytest.raises(fa.FaError):  # the backward takes d = 64 or 128
         fa.bwd(q, q, q, q, lse, q)
     q64 = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(ValueError):
