@@ -9,15 +9,22 @@ Prints one JSON line:
                holds for clock_mhz, the shader clock measured under the kernel, and the fraction
                of the MFMA peak at that clock
   cpu_baseline the CPU oracle timed on the host cores on a bounded sample of the same workload
-  sweep        the same measurement at the other sequence lengths of the metric (and d=128)
+  sweep        the same measurement at the other sequence lengths of the metric (T = 1024, 2048,
+               8192, 16384) and on the non-causal d=128 workload
   backward     fa_bwd (dQ, dK, dV from the forward's O and LSE) on the same workload: counted
-               TFLOP/s with the usual 2.5x-forward count, per-launch HIP events around both kernels
+               TFLOP/s with the usual 2.5x-forward count, per-launch HIP events around both kernels;
+               d128: the same on the non-causal d=128 workload
   sparse       fa_fwd_sparse at T=16384 (B4 H12 d64 causal) under a seeded block mask (25% of the
                128x64 blocks plus the diagonal ones): TFLOP/s over the visible (query, key) pairs
                and the time against the dense forward of the same shape
+  splitkv      fa_fwd_splitkv on decode shapes (1 and 16 queries after 16384 keys) against the HBM
+               roofline, and the T=16384 workload as 4 key shards plus fa_merge
+  fp8          fa_fwd_fp8 on E4M3 copies of the T=4096, 16384 and d=128 workloads against the FP8
+               MFMA peak, with fa_fwd on the bf16 inputs timed alongside
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c4] [--no-cpu-baseline]
-                       [--no-sweep] [--no-backward] [--only-backward]
+                       [--no-sweep] [--no-backward] [--only-backward] [--no-sparse] [--no-splitkv]
+                       [--no-fp8]
 """
 from __future__ import annotations
 
@@ -509,10 +516,16 @@ def main(argv=None):
 
     sweep = {}
     if not args.no_sweep:
-        for name in ("c3", "c5a", "c5b"):
+        from exact_tiled_attention_07_amd.inputs import Workload
+
+        # the metric's range of T at B4 H12 d64 causal: the workloads at T = 1024 and 16384, two
+        # points in between (seeded like the others), and the non-causal d = 128 workload
+        between = {"t2048": Workload("t2048_causal_B4_H12_T2048_d64", 4, 12, 2048, 64, True, seed=7),
+                   "t8192": Workload("t8192_causal_B4_H12_T8192_d64", 4, 12, 8192, 64, True, seed=8)}
+        for name in ("c3", "t2048", "c4", "t8192", "c5a", "c5b"):
             if name == args.workload:
                 continue
-            w2 = WORKLOADS[name]
+            w2 = between[name] if name in between else WORKLOADS[name]
             wms, kms, ex2 = time_workload(w2, max(5, args.steps // 5), max(2, args.warmup // 5), None)
             sweep[name] = {"workload": w2.name, "ms_per_step": round(wms, 5),
                            "tflops": round(w2.flops / (wms * 1e-3) / 1e12, 2),
