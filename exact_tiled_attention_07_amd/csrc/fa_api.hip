@@ -21,13 +21,15 @@ struct TileEntry {
   int d, block_m, block_n, waves;
   KernelFn causal_fn, full_fn;
   int lds_bytes;
+  int key_split;  // waves sharing one 32-query block, each on every key_split-th K/V tile
 };
 
-template <int D, int QB, int NW, int BN, int NSTAGE = 2>
+template <int D, int QB, int NW, int BN, int NSTAGE = 2, int KSPLIT = 1>
 constexpr TileEntry entry() {
-  using Cc = fa::Cfg<D, QB, NW, BN, true, NSTAGE>;
-  using Cf = fa::Cfg<D, QB, NW, BN, false, NSTAGE>;
-  return TileEntry{D, Cc::BM, BN, NW, &fa::fa_fwd_kernel<Cc>, &fa::fa_fwd_kernel<Cf>, Cc::LDS_BYTES};
+  using Cc = fa::Cfg<D, QB, NW, BN, true, NSTAGE, false, false, false, KSPLIT>;
+  using Cf = fa::Cfg<D, QB, NW, BN, false, NSTAGE, false, false, false, KSPLIT>;
+  return TileEntry{D, Cc::BM, BN, NW, &fa::fa_fwd_kernel<Cc>, &fa::fa_fwd_kernel<Cf>, Cc::LDS_BYTES,
+                   KSPLIT};
 }
 
 // Supported tile shapes. The first entry for each d is the default (see default_tile()).
@@ -38,6 +40,7 @@ const TileEntry kTiles[] = {
     entry<64, 2, 2, 64>(),   // d=64: 128 queries (2 waves x 64)
     entry<64, 2, 4, 64>(),   // d=64: 256 queries (4 waves x 64)
     entry<64, 1, 8, 64>(),   // d=64: 256 queries (8 waves x 32)
+    entry<64, 1, 4, 64, 2, 2>(),  // d=64: 64 queries, two waves per 32 queries splitting the keys
     entry<128, 1, 4, 64>(),  // d=128: 128 queries (4 waves x 32), 64-key tiles
     entry<128, 1, 2, 64>(),  // d=128: 64 x 64
 };
@@ -48,7 +51,17 @@ const TileEntry* find_tile(int d, int block_m, int block_n, int waves) {
   return nullptr;
 }
 
-const TileEntry* default_tile(int d, int /*T*/, int /*causal*/) {
+// Workgroups of the 128-query default below which short sequences take the key split: with fewer
+// than two such workgroups per compute unit the chip is under-filled and the last Q block of each
+// head (which visits every K/V tile of the head) sets the time; splitting its keys between two
+// waves halves that path and doubles the workgroups.
+constexpr int64_t kKeySplitBelow = 512;
+
+const TileEntry* default_tile(int d, int T, int64_t BH) {
+  if (d == 64 && (int64_t)((T + 127) / 128) * BH < kKeySplitBelow) {
+    const TileEntry* ks = find_tile(64, 64, 64, 4);
+    if (ks) return ks;
+  }
   for (const TileEntry& t : kTiles)
     if (t.d == d) return &t;
   return nullptr;
@@ -62,9 +75,9 @@ int check_sizes(int B, int H, int T, int d) {
   return FA_OK;
 }
 
-int resolve_tile(int d, int T, int causal, int block_m, int block_n, int waves, const TileEntry** out) {
+int resolve_tile(int d, int T, int64_t BH, int block_m, int block_n, int waves, const TileEntry** out) {
   if (block_m == 0 && block_n == 0 && waves == 0) {
-    *out = default_tile(d, T, causal);
+    *out = default_tile(d, T, BH);
   } else {
     if (block_m <= 0 || block_n <= 0 || waves <= 0) return FA_ERR_TILE;
     *out = find_tile(d, block_m, block_n, waves);
@@ -84,7 +97,7 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (rc != FA_OK) return rc;
   if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
   const TileEntry* tile = nullptr;
-  rc = resolve_tile(d, T, causal, block_m, block_n, waves, &tile);
+  rc = resolve_tile(d, T, (int64_t)B * H, block_m, block_n, waves, &tile);
   if (rc != FA_OK) return rc;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGNMENT;
   if ((uintptr_t)lse & 3u) return FA_ERR_ALIGNMENT;
@@ -484,7 +497,7 @@ int fa_fwd_plan(int B, int H, int T, int d, int causal, int block_m, int block_n
   int rc = check_sizes(B, H, T, d);
   if (rc != FA_OK) return rc;
   const TileEntry* tile = nullptr;
-  rc = resolve_tile(d, T, causal, block_m, block_n, waves, &tile);
+  rc = resolve_tile(d, T, (int64_t)B * H, block_m, block_n, waves, &tile);
   if (rc != FA_OK) return rc;
   fa_plan_info p;
   p.block_m = tile->block_m;
@@ -493,6 +506,7 @@ int fa_fwd_plan(int B, int H, int T, int d, int causal, int block_m, int block_n
   p.q_blocks = (T + tile->block_m - 1) / tile->block_m;
   p.grid = (long long)p.q_blocks * B * H;
   p.lds_bytes = tile->lds_bytes;
+  p.key_split = tile->key_split;
   // K/V tiles per Q block: up to the diagonal when causal, all of them otherwise.
   long long tiles_per_head = 0;
   for (int qb = 0; qb < p.q_blocks; ++qb) {
@@ -509,7 +523,7 @@ const char* fa_strerror(int status) {
     case FA_OK: return "ok";
     case FA_ERR_NULL: return "a required pointer is NULL";
     case FA_ERR_INVALID_ARG: return "invalid argument (size out of range, scale not finite and > 0, or overlapping buffers)";
-    case FA_ERR_UNSUPPORTED_D: return "unsupported head dimension (d must be 64 or 128; 64 for fa_bwd)";
+    case FA_ERR_UNSUPPORTED_D: return "unsupported head dimension (d must be 64 or 128)";
     case FA_ERR_ALIGNMENT: return "misaligned pointer (bf16 tensors need 16 bytes; lse and delta need 4)";
     case FA_ERR_HIP: return "HIP runtime error at kernel launch";
     case FA_ERR_TILE: return "tile shape not in the supported table";

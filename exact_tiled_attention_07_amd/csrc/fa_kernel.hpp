@@ -19,7 +19,10 @@
 //   - the softmax of one block runs while the matrix unit computes the next block's scores, the
 //     overlap of non-matrix work with matrix work that the cnblogs page describes for its third
 //     version ("最近在 V3 版本中");
-//   - the per-row logsumexp is written for a backward pass (STEP 4, note on training).
+//   - the per-row logsumexp is written for a backward pass (STEP 4, note on training);
+//   - for short sequences (few Q blocks) two waves may share one block of queries, each walking
+//     every other K/V block, and combine their (m, l, O) at the end with the log-space merge of
+//     partial results over disjoint key sets (ijyty.com FlashAttention article, section 2.1).
 //
 // gfx950 mapping (measured on the device, not taken from the pages):
 //   - v_mfma_f32_32x32x16_bf16 (32 cycles, 1024 flop/clk/SIMD). Lane l holds A row l%32 and
@@ -59,7 +62,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kSparseMaxFloor = -1.0e30f;  // running-max floor of the block-sparse path
 
 template <int D_, int QB_, int NW_, int BN_, bool CAUSAL_, int NSTAGE_, bool SPARSE_ = false,
-          bool RANGE_ = false, bool FEWQ_ = false>
+          bool RANGE_ = false, bool FEWQ_ = false, int KSPLIT_ = 1>
 struct Cfg {
   static constexpr int D = D_;        // head dim
   static constexpr int QB = QB_;      // 32-query column blocks per wave
@@ -78,12 +81,19 @@ struct Cfg {
   static_assert(!(SPARSE_ && RANGE_), "one tile selection at a time");
   // fewer queries than a workgroup holds (T < BM): waves without a query row skip the arithmetic
   static constexpr bool FEWQ = FEWQ_;
-  static constexpr int BM = 32 * QB * NW;           // queries per workgroup
+  // key split: KSPLIT waves share one block of queries; wave (block b, part p) visits the K/V tiles
+  // p, p + KSPLIT, ... of the block's range, and the parts are merged in log space at the end
+  static constexpr int KSPLIT = KSPLIT_;
+  static constexpr bool FLOORED = SPARSE_ || RANGE_ || KSPLIT_ > 1;  // a wave's row may see no key
+  static_assert(KSPLIT == 1 || (KSPLIT == 2 && QB == 1 && NW % 2 == 0 && !SPARSE_ && !RANGE_ && !FEWQ_),
+                "key split: two waves per 32-query block, dense forward only");
+  static constexpr int BM = 32 * QB * NW / KSPLIT;  // queries per workgroup
   static constexpr int THREADS = 64 * NW;
   static constexpr int ROW_BYTES = D * 2;           // one bf16 row of K or V
   static constexpr int CHUNKS = D / 8;              // 16-byte chunks per row
   static constexpr int TILE_BYTES = BN * ROW_BYTES; // one K (or V) tile
-  static constexpr int LDS_BYTES = 2 * NSTAGE * TILE_BYTES;  // K ring, then V ring
+  static constexpr int SLOT_BYTES = KSPLIT * TILE_BYTES;     // one ring buffer: the tiles of a step
+  static constexpr int LDS_BYTES = 2 * NSTAGE * SLOT_BYTES;  // K ring, then V ring
   static constexpr int LOADS = TILE_BYTES / (16 * THREADS);  // 16-byte loads per lane per tile
   static constexpr int KSTEPS = D / 16;             // k-steps of the score MFMA
   static constexpr int KB = BN / 32;                // 32-key blocks per tile
@@ -102,12 +112,14 @@ struct Cfg {
   static constexpr int MAX_FIRST = NS_QK + 2;
   static constexpr int MAX_LAST = NS - 3;
   static_assert(MAX_LAST >= MAX_FIRST, "slots for the row max");
-  static constexpr int VRING = NSTAGE * TILE_BYTES; // offset of the V ring
+  static constexpr int VRING = NSTAGE * SLOT_BYTES; // offset of the V ring
   static_assert(D == 64 || D == 128, "head dim");
   static_assert(BN % 32 == 0 && BN >= 32, "tile keys");
   static_assert(LOADS >= 1 && LOADS * 16 * THREADS == TILE_BYTES, "tile load split");
   static_assert(NSTAGE >= 2 && NSTAGE <= 4, "ring depth");
   static_assert(LDS_BYTES <= 65536, "static LDS of one workgroup");
+  // the merge of a key split exchanges acc (16*CB floats per lane), m and l of one wave per block
+  static_assert(KSPLIT == 1 || 256 * (16 * CB + 2) * (NW / KSPLIT) <= LDS_BYTES, "merge area");
 };
 
 template <int I, int N, class F>
@@ -258,7 +270,11 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   const int64_t head_off_k = (int64_t)bh * Tk * D;  // k and v rows of this head
   const char* kg = reinterpret_cast<const char*>(k + head_off_k);
   const char* vg = reinterpret_cast<const char*>(v + head_off_k);
-  const int qw0 = q0 + 32 * QB * w;  // first query of this wave
+  // with a key split, wave w holds query block w / KSPLIT and visits every KSPLIT-th tile from
+  // tile w % KSPLIT (both uniform per wave)
+  const int wq = C::KSPLIT == 1 ? w : w / C::KSPLIT;
+  const int part = C::KSPLIT == 1 ? 0 : w % C::KSPLIT;
+  const int qw0 = q0 + 32 * QB * wq;  // first query of this wave
   // With few queries (a key range for a handful of new queries) whole waves hold no query row:
   // they still copy their share of every tile and meet every barrier, but skip the MFMA and the
   // softmax (a wave-uniform branch; the barriers stay outside it).
@@ -299,10 +315,20 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   }
   const int t_begin = C::RANGE ? k_begin / BN : 0;  // first tile of the key range
   if constexpr (C::RANGE) n_tiles = max(0, min((k_end + BN - 1) / BN, n_cand) - t_begin);
+  // key split: n_tiles counts steps; step x copies tiles KSPLIT*x .. +KSPLIT-1 (clamped to the last
+  // one, a harmless re-copy) and this wave computes tile KSPLIT*x + part, which past n_cand-1 is a
+  // wholly masked tile (its keys are past the sequence: the ragged-end mask removes them all)
+  if constexpr (C::KSPLIT > 1) n_tiles = (n_cand + C::KSPLIT - 1) / C::KSPLIT;
   // (k_begin, k_end and t_begin are uniform; n_tiles stays a scalar)
   auto tile_at = [&](int x) -> int {
     if constexpr (C::SPARSE) return __builtin_amdgcn_readfirstlane((int)tlist[x]);
+    else if constexpr (C::KSPLIT > 1) return C::KSPLIT * x + part;
     else return t_begin + x;
+  };
+  // the tile copied into sub-buffer sub of step x's ring buffer
+  auto copy_tile = [&](int x, int sub) -> int {
+    if constexpr (C::KSPLIT > 1) return min(C::KSPLIT * x + sub, n_cand - 1);
+    else return tile_at(x);
   };
   if constexpr (C::LISTED) {
     if (n_tiles == 0) {  // no key visible to any row of the block: O = 0, LSE = -inf
@@ -322,7 +348,9 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
       return;
     }
   }
-  const int last_tile = tile_at(n_tiles - 1);
+  // the last tile holding keys (uniform over the workgroup) and its sub-buffer
+  const int last_tile = C::KSPLIT > 1 ? n_cand - 1 : tile_at(n_tiles - 1);
+  const int last_sub = C::KSPLIT > 1 ? last_tile % C::KSPLIT : 0;
   const bool tail_ragged = (last_tile + 1) * BN > Tk;
 
   // ---- HBM -> LDS copies of one K or V tile. Lane `lane` of load i fills 16 bytes of the 1 KiB
@@ -355,6 +383,11 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
       }
     }
   };
+  // the tiles of step x into the ring buffer at buf_off (one tile unless the keys are split)
+  auto dma_step = [&](const char* g, int x, int buf_off) {
+#pragma unroll
+    for (int sub = 0; sub < C::KSPLIT; ++sub) dma(g, copy_tile(x, sub), buf_off + sub * C::TILE_BYTES);
+  };
   // Zero the V rows at or past Tk of a ragged last tile, so a clamped copy of row Tk-1 can never
   // reach the output (their weights are 0; a non-finite input row would still give 0 * inf).
   auto zero_v_tail = [&](int buf_off) {
@@ -379,8 +412,8 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   // Prologue copies: K(0 .. NSTAGE-1) and V(0 .. NSTAGE-2) (clamped to the last tile).
 #pragma unroll
   for (int t = 0; t < C::NSTAGE; ++t) {
-    if (t < n_tiles) dma(kg, tile_at(t), buf_of(t) * C::TILE_BYTES);
-    if (t < C::NSTAGE - 1 && t < n_tiles) dma(vg, tile_at(t), C::VRING + buf_of(t) * C::TILE_BYTES);
+    if (t < n_tiles) dma_step(kg, t, buf_of(t) * C::SLOT_BYTES);
+    if (t < C::NSTAGE - 1 && t < n_tiles) dma_step(vg, t, C::VRING + buf_of(t) * C::SLOT_BYTES);
   }
 
   // ---- Q fragments straight into registers: B operand of S^T = K Q^T. Lane (n, hf) holds
@@ -397,9 +430,10 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   // ---- per-lane LDS byte addresses of the MFMA fragments (the buffer and the k-step / key block
   // parts are compile-time immediates).
   // K fragment (kb, s): row 32*kb + n, channels 16*s + 8*hf .. +7.
+  // (with a key split the wave's sub-buffer is folded in here)
   int k_off[KSTEPS];
 #pragma unroll
-  for (int s = 0; s < KSTEPS; ++s) k_off[s] = n * RB + swz<D>(n, 2 * s + hf) * 16;
+  for (int s = 0; s < KSTEPS; ++s) k_off[s] = part * C::TILE_BYTES + n * RB + swz<D>(n, 2 * s + hf) * 16;
   // V^T fragment (t, cb): lane l (group g = l/16, i = l%16) holds V^T row c(cb, l%32) at the 8
   // keys of its P^T slots, via two transposing reads of 4 keys each. Source lane i of a group
   // reads V row (16*t + 4*(g/2) + i/4 [+ 8]) at 4 channels starting at the column below.
@@ -414,7 +448,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
 #pragma unroll
       for (int rr = 0; rr < 2; ++rr) {
         const int r = 4 * gh + e_src + 8 * rr;
-        v_off[cb][rr] = r * RB + swz<D>(r, col >> 3) * 16 + (col & 7) * 2;
+        v_off[cb][rr] = part * C::TILE_BYTES + r * RB + swz<D>(r, col >> 3) * 16 + (col & 7) * 2;
       }
     }
   }
@@ -513,7 +547,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   vmem_wait<0>();
   __syncthreads();
   if (tail_ragged && n_tiles - 1 <= C::NSTAGE - 2) {  // the last V tile came with the prologue
-    zero_v_tail(C::VRING + buf_of(n_tiles - 1) * C::TILE_BYTES);
+    zero_v_tail(C::VRING + buf_of(n_tiles - 1) * C::SLOT_BYTES + last_sub * C::TILE_BYTES);
     __syncthreads();
   }
 #pragma unroll
@@ -525,7 +559,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 kf = read_k(buf_of(0) * C::TILE_BYTES, kb, s);
+        const bf16x8 kf = read_k(buf_of(0) * C::SLOT_BYTES, kb, s);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
           sa[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][s], sa[kb][qb], 0, 0, 0);
@@ -538,10 +572,10 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     float mx = -__builtin_inff();
     max_chunk(sa, qb, 0, 16, mx);
     m_run[qb] = wave_max_halves(mx) * scale_log2;  // dense: key 0 is visible to every row: finite
-    // block-sparse: a row may see no key of its first tile (or of any); a finite floor keeps
-    // exp2(s - m) at 0 for masked scores instead of NaN, and the floor is left behind (with
-    // alpha = 0) as soon as the row sees a key
-    if constexpr (C::LISTED) m_run[qb] = max_f32(m_run[qb], kSparseMaxFloor);
+    // block-sparse, key ranges, key split: a row may see no key of its first tile (or of any); a
+    // finite floor keeps exp2(s - m) at 0 for masked scores instead of NaN, and the floor is left
+    // behind (with alpha = 0) as soon as the row sees a key
+    if constexpr (C::FLOORED) m_run[qb] = max_f32(m_run[qb], kSparseMaxFloor);
   }
 
   // ---- one pipelined step: softmax + P.V of tile j (scores in s_cur, V at LDS offset VR) while
@@ -550,8 +584,8 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   auto step = [&](int j, int KR, int VR, int KW, int VW, f32x16 (&s_cur)[KB][QB],
                   f32x16 (&s_nxt)[KB][QB]) {
     // past the end: harmless re-copies of the last tile into a buffer nobody reads any more
-    dma(kg, tile_at(min(j + C::NSTAGE, n_tiles - 1)), KW);
-    dma(vg, tile_at(min(j + C::NSTAGE - 1, n_tiles - 1)), VW);
+    dma_step(kg, min(j + C::NSTAGE, n_tiles - 1), KW);
+    dma_step(vg, min(j + C::NSTAGE - 1, n_tiles - 1), VW);
 
     if (wave_active) {
       float neg_m[QB], lsum[QB], mx[QB], m_spec[QB], a_spec[QB];
@@ -669,7 +703,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     vmem_wait<2 * C::LOADS * (C::NSTAGE - 2)>();
     __syncthreads();
     if (tail_ragged && j + 2 == n_tiles && n_tiles - 1 > C::NSTAGE - 2) {  // V(n-1) just landed
-      zero_v_tail(C::VRING + buf_of(n_tiles - 1) * C::TILE_BYTES);
+      zero_v_tail(C::VRING + buf_of(n_tiles - 1) * C::SLOT_BYTES + last_sub * C::TILE_BYTES);
       __syncthreads();
     }
   };
@@ -701,8 +735,8 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   auto run_step = [&](int j, f32x16 (&s_cur)[KB][QB], f32x16 (&s_nxt)[KB][QB]) {
     const int r1 = nxt(ring_j);                       // (j+1) % NSTAGE
     const int rv = C::NSTAGE == 2 ? r1 : nxt(r1);     // (j+NSTAGE-1) % NSTAGE
-    step(j, r1 * C::TILE_BYTES, C::VRING + ring_j * C::TILE_BYTES, ring_j * C::TILE_BYTES,
-         C::VRING + rv * C::TILE_BYTES, s_cur, s_nxt);
+    step(j, r1 * C::SLOT_BYTES, C::VRING + ring_j * C::SLOT_BYTES, ring_j * C::SLOT_BYTES,
+         C::VRING + rv * C::SLOT_BYTES, s_cur, s_nxt);
     ring_j = r1;
   };
   const int n_steps = n_tiles - 1;  // pipelined steps; the last tile is finished by last_step
@@ -720,20 +754,51 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     run_step(j, sa, sb);
     run_step(j + 1, sb, sa);
   }
-  last_step(C::VRING + ring_j * C::TILE_BYTES, sa);
+  last_step(C::VRING + ring_j * C::SLOT_BYTES, sa);
   // Copies issued by the last steps may still be in flight (re-copies past the end); they must land
   // before this workgroup's LDS can be handed to another one.
   vmem_wait<0>();
   if (!wave_active) return;  // no query row to store
+  float l_tot[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) l_tot[qb] = wave_sum_halves(l_run[qb]);
+
+  // ---- key split: the two waves of a query block saw disjoint sets of keys; the second hands its
+  // (acc, m, l) to the first through LDS (the rings are free once every wave is past its last
+  // tile), which merges them in log space: m = max(m0, m1), acc = acc0 2^(m0-m) + acc1 2^(m1-m),
+  // l likewise. Lane (n, hf) of both waves holds the same query and channels.
+  if constexpr (C::KSPLIT > 1) {
+    constexpr int NX = 16 * CB + 2;  // floats per lane: acc, m, l
+    float* xch = reinterpret_cast<float*>(smem) + wq * NX * 64 + lane;
+    __syncthreads();
+    if (part != 0) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xch[(16 * cb + r) * 64] = acc[cb][0][r];
+      xch[(16 * CB) * 64] = m_run[0];
+      xch[(16 * CB + 1) * 64] = l_tot[0];
+    }
+    __syncthreads();
+    if (part != 0) return;
+    const float m1 = xch[(16 * CB) * 64], l1 = xch[(16 * CB + 1) * 64];
+    const float m = max_f32(m_run[0], m1);
+    const float a0 = __builtin_amdgcn_exp2f(m_run[0] - m), a1 = __builtin_amdgcn_exp2f(m1 - m);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[cb][0][r] = acc[cb][0][r] * a0 + xch[(16 * cb + r) * 64] * a1;
+    l_tot[0] = l_tot[0] * a0 + l1 * a1;
+    m_run[0] = m;
+  }
 
   // ---- epilogue: O = acc / l, rounded once to bf16; LSE = ln2 * (m + log2 l).
   // Lane (n, hf) of channel block cb holds channels (D/2)*hf + 16*cb + r, r = 0..15, in order.
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qw0 + 32 * qb + n;
-    const float l_tot = wave_sum_halves(l_run[qb]);
-    float inv = 1.0f / l_tot;
-    if constexpr (C::LISTED) inv = l_tot > 0.0f ? inv : 0.0f;  // a row that saw no key: O = 0
+    float inv = 1.0f / l_tot[qb];
+    if constexpr (C::LISTED) inv = l_tot[qb] > 0.0f ? inv : 0.0f;  // a row that saw no key: O = 0
     if (row < T) {
       if constexpr (C::RANGE) {  // partial output of a key range: fp32
         float* orow = reinterpret_cast<float*>(o) + head_off + (int64_t)row * D;
@@ -760,8 +825,8 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
           }
         }
       }
-      float lse_row = (m_run[qb] + __log2f(l_tot)) * kLn2;
-      if constexpr (C::LISTED) lse_row = l_tot > 0.0f ? lse_row : -__builtin_inff();
+      float lse_row = (m_run[qb] + __log2f(l_tot[qb])) * kLn2;
+      if constexpr (C::LISTED) lse_row = l_tot[qb] > 0.0f ? lse_row : -__builtin_inff();
       if (hf == 0) lse[(int64_t)bh * T + row] = lse_row;
     }
   }

@@ -91,6 +91,9 @@ typedef struct fa_plan_info {
   long long grid;  /* workgroups launched: q_blocks * B * H (one per (Q block, batch*head)) */
   int lds_bytes;   /* LDS per workgroup: double-buffered K and V tiles */
   long long kv_tiles; /* K/V tiles processed by all workgroups (fully masked ones skipped) */
+  int key_split;   /* 1, or 2: two waves share each 32-query block, each taking every other K/V tile,
+                      and merge their partial results in log space (the default for short
+                      sequences at d = 64, when ceil(T/128)*B*H < 512) */
 } fa_plan_info;
 
 /*

@@ -122,6 +122,19 @@ def test_plan_default_and_tile_counts():
     assert fa.plan(0, 12, 1000, 64, True)["grid"] == 0
 
 
+def test_plan_key_split_for_short_sequences():
+    # d = 64 problems whose 128-query grid is below 512 workgroups take the key split
+    c3 = fa.plan(4, 12, 1024, 64, True)  # 8 x 48 = 384 workgroups of 128 queries
+    assert (c3["key_split"], c3["block_m"], c3["waves"], c3["lds_bytes"]) == (2, 64, 4, 65536)
+    assert c3["grid"] == 16 * 48
+    assert fa.plan(2, 12, 1000, 64, True)["key_split"] == 2
+    assert fa.plan(4, 12, 2048, 64, True)["key_split"] == 1   # 16 x 48 = 768
+    assert fa.plan(4, 12, 4096, 64, True)["key_split"] == 1
+    assert fa.plan(1, 1, 8, 128, True)["key_split"] == 1      # d = 128 never splits
+    assert fa.plan(4, 12, 4096, 64, True, 64, 64, 4)["key_split"] == 2  # forced
+    assert fa.plan(1, 1, 8, 64, True, 128, 64, 4)["key_split"] == 1
+
+
 def test_plan_errors():
     with pytest.raises(fa.FaError) as e:
         fa.plan(1, 1, 8, 80)

@@ -96,8 +96,22 @@ def test_configs_sampled(name):
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("T", [1, 2, 31, 63, 64, 65, 127, 129, 255, 257, 1000])
 def test_ragged_and_tiny_lengths(T, causal, d):
+    # small problems: at d = 64 the default launch is the key split (two waves per query block)
     qb, kb, vb = make_qkv(1, 3, T, d, seed=1000 + T + d)
     full_check(qb, kb, vb, causal, 1.0 / math.sqrt(d), f"T={T} d={d}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("T", [1, 2, 63, 64, 65, 127, 128, 129, 191, 255, 257, 1000])
+def test_ragged_and_tiny_lengths_both_launches(T, causal):
+    # the same small problems through the 128-query launch and through the key split, forced
+    qb, kb, vb = make_qkv(2, 2, T, 64, seed=5000 + T)
+    o_ref, lse_ref = oracle.attention_fwd(qb, kb, vb, causal, 0.125)
+    for bm, bn, w in ((128, 64, 4), (64, 64, 4)):
+        o, lse = run_gpu_ex(qb, kb, vb, causal, 0.125, bm, bn, w)
+        assert_parity(compare(o, lse, o_ref, lse_ref), f"T={T} tile {bm}x{bn}x{w}")
+        if causal:  # row 0 sees key 0 alone: O[0] = V[0] bit for bit, whichever wave holds it
+            np.testing.assert_array_equal(o[:, :, 0, :], bf16_bits_to_f32(vb)[:, :, 0, :])
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -156,7 +170,8 @@ def test_one_hot_values_expose_p():
 @pytest.mark.parametrize("d", [64, 128])
 def test_every_tile_shape(d):
     from exact_tiled_attention_07_amd.fa import lib  # noqa: F401  (library must be loaded)
-    shapes = {64: [(128, 64, 4), (128, 128, 4), (64, 64, 2), (128, 64, 2), (256, 64, 4), (256, 64, 8)],
+    shapes = {64: [(128, 64, 4), (128, 128, 4), (64, 64, 2), (128, 64, 2), (256, 64, 4), (256, 64, 8),
+                   (64, 64, 4)],
               128: [(128, 64, 4), (64, 64, 2)]}[d]
     qb, kb, vb = make_qkv(2, 3, 1000, d, seed=31 + d)
     scale = 1.0 / math.sqrt(d)
@@ -168,7 +183,8 @@ def test_every_tile_shape(d):
             assert_parity(compare(o, lse, o_ref, lse_ref), f"tile {bm}x{bn}x{w}")
 
 
-def test_writes_stay_inside_outputs_and_are_deterministic():
+@pytest.mark.parametrize("tile", [None, (128, 64, 4), (64, 64, 4)])
+def test_writes_stay_inside_outputs_and_are_deterministic(tile):
     B, H, T, d = 2, 3, 333, 64
     qb, kb, vb = make_qkv(B, H, T, d, seed=41)
     q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
@@ -178,12 +194,17 @@ def test_writes_stay_inside_outputs_and_are_deterministic():
     l_big = torch.full((nl + 2 * guard,), float("nan"), dtype=torch.float32, device=DEV)
     o = o_big[guard:guard + n].view(B, H, T, d)
     lse = l_big[guard:guard + nl].view(B, H, T)
-    fa.fwd(q, k, v, causal=True, out=o, lse=lse)
+
+    def run(**kw):
+        if tile is None:
+            return fa.fwd(q, k, v, causal=True, **kw)
+        return fa.fwd_ex(q, k, v, *tile, causal=True, **kw)
+    run(out=o, lse=lse)
     torch.cuda.synchronize()
     assert torch.isnan(o_big[:guard].float()).all() and torch.isnan(o_big[guard + n:].float()).all()
     assert torch.isnan(l_big[:guard]).all() and torch.isnan(l_big[guard + nl:]).all()
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-    o2, lse2 = fa.fwd(q, k, v, causal=True)
+    o2, lse2 = run()
     torch.cuda.synchronize()
     assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
 
