@@ -79,7 +79,8 @@ def test_sparse_all_ones_equals_dense(causal, d):
     q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
     ones = torch.ones(fa.sparse_mask_shape(1000, 1), dtype=torch.uint8, device=DEV)
     o_s, l_s = fa.fwd_sparse(q, k, v, ones, causal=causal)
-    o_d, l_d = fa.fwd(q, k, v, causal=causal)
+    # the dense forward with the same 128 x 64 tiles (fa_fwd itself takes the key split at this size)
+    o_d, l_d = fa.fwd_ex(q, k, v, 128, 64, 4, causal=causal)
     torch.cuda.synchronize()
     assert torch.equal(o_s.view(torch.int16), o_d.view(torch.int16))
     assert torch.equal(l_s, l_d)
