@@ -526,7 +526,12 @@ def main(argv=None):
             if name == args.workload:
                 continue
             w2 = between[name] if name in between else WORKLOADS[name]
-            wms, kms, ex2 = time_workload(w2, max(5, args.steps // 5), max(2, args.warmup // 5), None)
+            # short launches get more steps, so warm-up and timing each span about 25 ms of work
+            # (the shader clock rises over the first milliseconds of load)
+            est_s = w2.flops / 800e12
+            n_t = min(2000, max(5, args.steps // 5, math.ceil(0.025 / est_s)))
+            n_w = min(2000, max(2, args.warmup // 5, math.ceil(0.025 / est_s)))
+            wms, kms, ex2 = time_workload(w2, n_t, n_w, None)
             sweep[name] = {"workload": w2.name, "ms_per_step": round(wms, 5),
                            "tflops": round(w2.flops / (wms * 1e-3) / 1e12, 2),
                            "kernel_tflops": round(w2.flops / (kms * 1e-3) / 1e12, 2),
