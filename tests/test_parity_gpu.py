@@ -92,6 +92,21 @@ def test_configs_sampled(name):
         np.testing.assert_array_equal(o[:, :, 0, :], bf16_bits_to_f32(vb)[:, :, 0, :])
 
 
+@pytest.mark.parametrize("causal", [True, False])
+def test_key_split_long_sequence(causal):
+    # two heads of T = 12289: the default launch is the key split (97 x 2 workgroups of 128 queries
+    # would be too few), whose waves then walk 97 tiles each; sampled rows against the oracle
+    B, H, T = 1, 2, 12289
+    assert fa.plan(B, H, T, 64, causal)["key_split"] == 2
+    qb, kb, vb = make_qkv(B, H, T, 64, seed=77, sigma=2.0)
+    o, lse = run_gpu(qb, kb, vb, causal, 0.125)
+    rows = sample_rows(B, H, T, 600, seed=78)
+    o_ref, lse_ref = oracle.attention_rows(qb, kb, vb, causal, 0.125, rows)
+    stats = compare(o.reshape(-1, 64)[rows], lse.reshape(-1)[rows], o_ref, lse_ref)
+    say(f"[gpu] key split T={T} causal={causal} {stats}")
+    assert_parity(stats, f"key split T={T}")
+
+
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("T", [1, 2, 31, 63, 64, 65, 127, 129, 255, 257, 1000])
