@@ -87,3 +87,8 @@ def test_tolerance_reading():
     # 0.014 literal; 0.0155 <= ulp(3)=2^-6; 0.031 <= ulp(5)=2^-5; 0.032 > 2^-5 fails; 0.016 at |1| fails
     assert s["n_ulp_clause"] == 2 and s["n_fail_o"] == 2
     assert math.isclose(O_TOL, 1.5e-2)
+
+
+def test_page_claims_are_context_only():
+    assert bench.PAGE_CLAIMS and all({"claim", "hardware", "source"} <= set(c) for c in bench.PAGE_CLAIMS)
+    assert not any("MI355X" == c["hardware"] for c in bench.PAGE_CLAIMS)
