@@ -14,6 +14,10 @@
 //     E4M3 (round to nearest even) for the second product, the one rounding this path adds;
 //   - output: O^T += V^T P^T on the same MFMA; at the end O = acc * v_descale / l, rounded once to
 //     bf16, and LSE = ln 2 * (m + log2 l - 8).
+//   - one score set per wave (the scores, softmax and P.V of a tile in turn): the kernel is bound by
+//     the softmax's VALU work, so it keeps registers low (116 VGPRs at d = 64: four waves per SIMD,
+//     164 at d = 128: three) and lets the resident waves overlap each other, rather than holding a
+//     second score set to overlap the next tile's scores inside a wave (182 VGPRs, two waves).
 //
 // gfx950 mapping (measured on the device with one-off probes):
 //   - v_mfma_f32_32x32x64_f8f6f4 (OCP E4M3 when both format fields are 0): lane l holds 32 bytes of
@@ -142,12 +146,9 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_fp8_kernel(
       *reinterpret_cast<u32x4*>(vl + r * RB + (idx % C::CHUNKS) * 16) = u32x4{0u, 0u, 0u, 0u};
     }
   };
-  const int ring0 = (n_tiles - 1) & 1;  // see fa_fwd_kernel: the paired steps start at buffer 0
-  auto buf_of = [&](int t) { return (t + ring0) & 1; };
 
-  dma(kg, 0, buf_of(0) * C::TILE_BYTES);
-  dma(vg, 0, C::VRING + buf_of(0) * C::TILE_BYTES);
-  if (n_tiles > 1) dma(kg, 1, buf_of(1) * C::TILE_BYTES);
+  dma(kg, 0, 0);
+  dma(vg, 0, C::VRING);
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane (n, hf) holds query qw0 + n, channels
   // 64*s + 32*hf .. +31 of k-step s.
@@ -197,8 +198,8 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_fp8_kernel(
   f32x16 acc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x16{};
-  float m_run, l_run = 0.0f, alpha = 1.0f;
-  f32x16 sa[KB], sb[KB];
+  float m_run = kSparseMaxFloor, l_run = 0.0f;
+
 
   auto scores = [&](int KR, f32x16 (&s_out)[KB]) {
 #pragma unroll
@@ -256,74 +257,40 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_fp8_kernel(
     for (int cb = 0; cb < CB; ++cb) acc[cb] = mfma_e4m3(read_v(VR, cb), pf, acc[cb]);
   };
 
-  // ---- prologue: S(0) and its row max
+  // ---- one K/V tile per step: its scores, the online softmax and P.V. One score set only, so
+  // that more waves fit on a SIMD; the copies of tile j+1 run during step j.
   vmem_wait<0>();
   __syncthreads();
   if (tail_ragged && n_tiles == 1) {
-    zero_v_tail(C::VRING + buf_of(0) * C::TILE_BYTES);
+    zero_v_tail(C::VRING);
     __syncthreads();
   }
-  scores(buf_of(0) * C::TILE_BYTES, sa);
-  __syncthreads();  // every wave has read K(0) before K(2) is copied into its buffer
-  if (needs_mask(0)) mask_tile(sa, 0);
-  // a row always sees key 0 of its first tile (causal: key 0 <= every query), so m is finite
-  m_run = row_max(sa);
-
-  // ---- step j: S(j+1) on the MFMA while the softmax of tile j runs, then P(j) V(j).
-  auto step = [&](int j, int KR, int VR, int KW, int VW, f32x16 (&s_cur)[KB], f32x16 (&s_nxt)[KB]) {
-    dma(kg, min(j + 2, n_tiles - 1), KW);
-    dma(vg, j + 1, VW);
-    scores(KR, s_nxt);
-    l_run *= alpha;
+  for (int j = 0; j < n_tiles; ++j) {
+    const int buf = j & 1;
+    if (j + 1 < n_tiles) {
+      dma(kg, j + 1, (buf ^ 1) * C::TILE_BYTES);
+      dma(vg, j + 1, C::VRING + (buf ^ 1) * C::TILE_BYTES);
+    }
+    f32x16 s[KB];
+    scores(buf * C::TILE_BYTES, s);
+    if (needs_mask(j)) mask_tile(s, j);
+    const float m_new = max_f32(m_run, row_max(s));
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    m_run = m_new;
     i32x8 pf;
-    l_run += softmax_pack(s_cur, pf);
-    const bool need_rescale = __builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0;
-    if (need_rescale) {
+    l_run = l_run * alpha + softmax_pack(s, pf);
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
     }
-    pv(VR, pf);
-    if (needs_mask(j + 1)) mask_tile(s_nxt, j + 1);
-    const float m_new = max_f32(m_run, row_max(s_nxt));
-    alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    pv(C::VRING + buf * C::TILE_BYTES, pf);
     vmem_wait<0>();
     __syncthreads();
     if (tail_ragged && j + 2 == n_tiles) {  // V(n-1) just landed
-      zero_v_tail(C::VRING + buf_of(n_tiles - 1) * C::TILE_BYTES);
+      zero_v_tail(C::VRING + ((j + 1) & 1) * C::TILE_BYTES);
       __syncthreads();
     }
-  };
-  int ring_j = ring0;
-  auto run_step = [&](int j, f32x16 (&s_cur)[KB], f32x16 (&s_nxt)[KB]) {
-    const int r1 = ring_j ^ 1;
-    step(j, r1 * C::TILE_BYTES, C::VRING + ring_j * C::TILE_BYTES, ring_j * C::TILE_BYTES,
-         C::VRING + r1 * C::TILE_BYTES, s_cur, s_nxt);
-    ring_j = r1;
-  };
-  const int n_steps = n_tiles - 1;
-  int j0 = 0;
-  if (n_steps & 1) {
-    run_step(0, sa, sb);
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) sa[kb] = sb[kb];
-    j0 = 1;
   }
-  ring_j = 0;
-  for (int j = j0; j < n_steps; j += 2) {
-    run_step(j, sa, sb);
-    run_step(j + 1, sb, sa);
-  }
-  // ---- last tile: softmax and P.V only
-  {
-    l_run *= alpha;
-    i32x8 pf;
-    l_run += softmax_pack(sa, pf);
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) acc[cb] *= alpha;
-    pv(C::VRING + ring_j * C::TILE_BYTES, pf);
-  }
-  vmem_wait<0>();
 
   // ---- epilogue: O = acc * v_descale / l (the 2^8 of P cancels against l), rounded to bf16;
   // LSE = ln 2 * (m + log2 l - 8). Lane (n, hf) holds channels 32*cb + 8*a + 4*hf + 0..3 in
