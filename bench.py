@@ -10,7 +10,7 @@ Prints one JSON line:
                of the MFMA peak at that clock
   cpu_baseline the CPU oracle timed on the host cores on a bounded sample of the same workload
   sweep        the same measurement at the other sequence lengths of the metric (T = 1024, 2048,
-               8192, 16384) and on the non-causal d=128 workload
+               8192, 16384) and on the d=128 workload (non-causal, and its causal variant)
   backward     fa_bwd (dQ, dK, dV from the forward's O and LSE) on the same workload: counted
                TFLOP/s with the usual 2.5x-forward count, per-launch HIP events around both kernels;
                d128: the same on the non-causal d=128 workload
@@ -536,10 +536,11 @@ def main(argv=None):
         from exact_tiled_attention_07_amd.inputs import Workload
 
         # the metric's range of T at B4 H12 d64 causal: the workloads at T = 1024 and 16384, two
-        # points in between (seeded like the others), and the non-causal d = 128 workload
+        # points in between (seeded like the others), and the d = 128 workload with its causal variant
         between = {"t2048": Workload("t2048_causal_B4_H12_T2048_d64", 4, 12, 2048, 64, True, seed=7),
-                   "t8192": Workload("t8192_causal_B4_H12_T8192_d64", 4, 12, 8192, 64, True, seed=8)}
-        for name in ("c3", "t2048", "c4", "t8192", "c5a", "c5b"):
+                   "t8192": Workload("t8192_causal_B4_H12_T8192_d64", 4, 12, 8192, 64, True, seed=8),
+                   "c5b_causal": Workload("c5b_causal_B4_H16_T8192_d128", 4, 16, 8192, 128, True, seed=9)}
+        for name in ("c3", "t2048", "c4", "t8192", "c5a", "c5b", "c5b_causal"):
             if name == args.workload:
                 continue
             w2 = between[name] if name in between else WORKLOADS[name]
