@@ -1,0 +1,102 @@
+"""Randomised pins of the CPU oracle (hypothesis): shapes, scales and input magnitudes drawn at random,
+each case checked against facts that do not come from the oracle itself.
+
+- the library: scipy's softmax and logsumexp on the masked fp64 score matrix (learn-llm.fim.ai
+  "手写 FlashAttention：拆开 SDPA 这个黑盒", STEP 1 and STEP 3 define the scores, the row softmax and the
+  causal mask);
+- shift invariance: adding one vector u to every key moves row i's scores by scale q_i . u, leaves O
+  unchanged and moves LSE by that amount (the max subtraction of STEP 2 makes the result independent
+  of a per-row constant);
+- the backward: PyTorch float64 autograd through a plain softmax attention;
+- the log-space merge of a random partition of the keys into ranges equals the whole (ijyty.com
+  FlashAttention article, section 2.1).
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+from hypothesis import HealthCheck, given, settings, strategies as st
+
+import oracle
+from exact_tiled_attention_07_amd.inputs import bf16_bits_from_f32, bf16_bits_to_f32
+
+SETTINGS = settings(max_examples=40, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
+
+
+def bf16_inputs(rng, B, H, T, d, sigma):
+    """bf16 bit patterns of N(0, sigma^2) draws (the widening to float64 is exact)."""
+    return [bf16_bits_from_f32((rng.standard_normal((B, H, T, d)) * sigma).astype(np.float32)) for _ in range(3)]
+
+
+def widen(bits):
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+shapes = st.tuples(st.integers(1, 2), st.integers(1, 3), st.integers(1, 40), st.sampled_from([1, 3, 8, 16, 64]))
+
+
+@SETTINGS
+@given(shape=shapes, causal=st.booleans(), scale=st.floats(0.01, 2.0), sigma=st.floats(0.1, 4.0),
+       seed=st.integers(0, 2 ** 31 - 1))
+def test_forward_equals_library_softmax(shape, causal, scale, sigma, seed):
+    B, H, T, d = shape
+    qb, kb, vb = bf16_inputs(np.random.default_rng(seed), B, H, T, d, sigma)
+    scale = float(np.float32(scale))
+    o, lse = oracle.attention_fwd(qb, kb, vb, causal, scale)
+    s = scale * np.matmul(widen(qb), np.swapaxes(widen(kb), -1, -2))
+    if causal:
+        s = np.where(np.triu(np.ones((T, T), dtype=bool), 1), -np.inf, s)
+    P = scipy.special.softmax(s, axis=-1)
+    np.testing.assert_allclose(o, np.matmul(P, widen(vb)), rtol=1e-10, atol=1e-10 * max(1.0, sigma))
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(s, axis=-1), rtol=1e-12, atol=1e-10)
+
+
+@SETTINGS
+@given(shape=shapes, causal=st.booleans(), seed=st.integers(0, 2 ** 31 - 1), shift=st.integers(-8, 8))
+def test_forward_key_shift_invariance(shape, causal, seed, shift):
+    B, H, T, d = shape
+    rng = np.random.default_rng(seed)
+    qb, kb, vb = bf16_inputs(rng, B, H, T, d, 1.0)
+    # u = shift * 2^-3 in every channel: k + u stays exactly representable in float64 (bf16 inputs
+    # widen exactly), so the float64 entry point sees the shifted keys without rounding
+    u = shift / 8.0
+    q, k, v = widen(qb), widen(kb), widen(vb)
+    o0, l0 = oracle.attention_fwd_f64(q, k, v, causal, 0.5)
+    o1, l1 = oracle.attention_fwd_f64(q, k + u, v, causal, 0.5)
+    np.testing.assert_allclose(o1, o0, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(l1, l0 + 0.5 * u * q.sum(axis=-1), rtol=1e-12, atol=1e-10)
+
+
+@SETTINGS
+@given(shape=st.tuples(st.integers(1, 2), st.integers(1, 2), st.integers(1, 24), st.sampled_from([2, 8, 16])),
+       causal=st.booleans(), seed=st.integers(0, 2 ** 31 - 1))
+def test_backward_equals_autograd(shape, causal, seed):
+    B, H, T, d = shape
+    rng = np.random.default_rng(seed)
+    q, k, v, do = (rng.standard_normal((B, H, T, d)) for _ in range(4))
+    scale = 1.0 / math.sqrt(d)
+    dq, dk, dv, delta = oracle.attention_bwd_f64(q, k, v, do, causal, scale)
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    s = torch.matmul(tq, tk.transpose(-1, -2)) * scale
+    if causal:
+        s = s.masked_fill(torch.triu(torch.ones(T, T, dtype=torch.bool), 1), float("-inf"))
+    o = torch.matmul(torch.softmax(s, dim=-1), tv)
+    o.backward(torch.tensor(do, dtype=torch.float64))
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(mine, ref.numpy(), rtol=1e-9, atol=1e-11)
+    np.testing.assert_allclose(delta, (o.detach().numpy() * do).sum(-1), rtol=1e-11, atol=1e-12)
+
+
+@SETTINGS
+@given(T=st.integers(1, 50), n_cuts=st.integers(0, 4), causal=st.booleans(), seed=st.integers(0, 2 ** 31 - 1))
+def test_merge_of_a_random_key_partition(T, n_cuts, causal, seed):
+    rng = np.random.default_rng(seed)
+    qb, kb, vb = bf16_inputs(rng, 1, 2, T, 8, 1.5)
+    cuts = sorted(set(rng.integers(0, T + 1, n_cuts).tolist()) | {0, T})
+    parts = [oracle.attention_fwd_cross(qb, kb, vb, causal, 0.35, a, b) for a, b in zip(cuts[:-1], cuts[1:])]
+    o, lse = oracle.merge_partials(np.stack([p[0] for p in parts]), np.stack([p[1] for p in parts]))
+    o_ref, lse_ref = oracle.attention_fwd(qb, kb, vb, causal, 0.35)
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-12)
