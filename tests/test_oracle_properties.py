@@ -14,7 +14,6 @@ each case checked against facts that do not come from the oracle itself.
 import math
 
 import numpy as np
-import pytest
 import scipy.special
 import torch
 from hypothesis import HealthCheck, given, settings, strategies as st
