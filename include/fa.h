@@ -66,6 +66,11 @@ typedef enum fa_status {
  *   causal   nonzero: query i sees keys 0..i (the causal mask); zero: it sees all T keys
  *   scale    finite and > 0; the scores are scale * q.k (1/sqrt(d) for standard attention)
  *   stream   hipStream_t to launch on (NULL: default stream)
+ * The launch depends on the sizes (fa_fwd_plan reports it): 128 queries per workgroup, or, at d = 64
+ * when ceil(T/128)*B*H < 512, the key split: two waves per 32-query block each take every other K/V
+ * tile and merge their partial results in log space (ijyty.com FlashAttention article, section
+ * 2.1). Both give the exact result up to rounding order; a fixed problem always takes the same
+ * launch, so repeated calls are bit-identical.
  * Returns FA_OK or a negative fa_status.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int T,
@@ -73,7 +78,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 
 /*
  * fa_fwd_ex — fa_fwd with the tile shape forced, for the tile-shape study.
- *   block_m  query rows per workgroup (a multiple of 32 * waves)
+ *   block_m  query rows per workgroup (32 * waves, 64 * waves per wave with two 32-query blocks, or
+ *            16 * waves for the key split, which fa_fwd_ex(..., 64, 64, 4) selects)
  *   block_n  keys per K/V tile staged in LDS
  *   waves    64-lane wavefronts per workgroup
  * The supported (d, block_m, block_n, waves) combinations are those fa_fwd_plan accepts; any other
