@@ -78,8 +78,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
 
 /*
  * fa_fwd_ex — fa_fwd with the tile shape forced, for the tile-shape study.
- *   block_m  query rows per workgroup (32 * waves, 64 * waves per wave with two 32-query blocks, or
- *            16 * waves for the key split, which fa_fwd_ex(..., 64, 64, 4) selects)
+ *   block_m  query rows per workgroup: 32 * waves (one 32-query block per wave), 64 * waves (two per
+ *            wave) or 16 * waves (the key split, two waves per block: fa_fwd_ex(..., 64, 64, 4))
  *   block_n  keys per K/V tile staged in LDS
  *   waves    64-lane wavefronts per workgroup
  * The supported (d, block_m, block_n, waves) combinations are those fa_fwd_plan accepts; any other
