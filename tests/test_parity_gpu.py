@@ -92,6 +92,26 @@ def test_configs_sampled(name):
         np.testing.assert_array_equal(o[:, :, 0, :], bf16_bits_to_f32(vb)[:, :, 0, :])
 
 
+def test_many_heads_short_sequences():
+    # 2048 heads of T = 100 (a grid of 2048 x 1 workgroups of 128 queries), and of T = 30 with the
+    # key split (ceil(30/128) x 64 heads < 512), every row checked
+    for B, H, T in ((32, 64, 100), (4, 16, 30)):
+        qb, kb, vb = make_qkv(B, H, T, 64, seed=B + H + T)
+        full_check(qb, kb, vb, True, 0.125, f"B{B} H{H} T{T}")
+
+
+def test_one_head_very_long_sequence():
+    # one head of T = 65536 (512 Q blocks, the last one walks 1024 K/V tiles), sampled rows
+    B, H, T = 1, 1, 65536
+    qb, kb, vb = make_qkv(B, H, T, 64, seed=65)
+    o, lse = run_gpu(qb, kb, vb, True, 0.125)
+    rows = sample_rows(B, H, T, 300, seed=66)
+    o_ref, lse_ref = oracle.attention_rows(qb, kb, vb, True, 0.125, rows)
+    stats = compare(o.reshape(-1, 64)[rows], lse.reshape(-1)[rows], o_ref, lse_ref)
+    say(f"[gpu] T={T} {stats}")
+    assert_parity(stats, f"T={T}")
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_key_split_long_sequence(causal):
     # two heads of T = 12289: the default launch is the key split (97 x 2 workgroups of 128 queries
