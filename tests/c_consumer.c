@@ -1,0 +1,146 @@
+/*
+ * A plain C99 program that uses libfa.so through include/fa.h and the HIP runtime's C API only
+ * (no Python, no PyTorch): the test that the boundary is usable as a C library.
+ *
+ *   c_consumer host
+ *       argument checks, status strings, fa_fwd_plan and the empty problem; no GPU call is made.
+ *   c_consumer fwd IN OUT B H T d causal scale
+ *       IN holds q, k, v as bf16 bit patterns ([B,H,T,d] each, in that order). The program copies
+ *       them to device memory, runs fa_fwd on a stream of its own, and writes o (bf16 bits) then
+ *       lse (fp32) to OUT.
+ * Exit status 0 on success; anything else prints what failed.
+ */
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <hip/hip_runtime_api.h>
+
+#include "fa.h"
+
+#define CHECK(cond, ...)                  \
+  do {                                    \
+    if (!(cond)) {                        \
+      fprintf(stderr, "c_consumer: ");    \
+      fprintf(stderr, __VA_ARGS__);       \
+      fprintf(stderr, "\n");              \
+      exit(2);                            \
+    }                                     \
+  } while (0)
+
+#define HIP(call)                                                                          \
+  do {                                                                                     \
+    hipError_t e_ = (call);                                                                \
+    CHECK(e_ == hipSuccess, "%s failed: %s", #call, hipGetErrorString(e_));                \
+  } while (0)
+
+static int host_checks(void) {
+  /* fake, aligned, distinct addresses: every call below fails validation or is empty, so none is
+   * dereferenced and nothing is launched */
+  char* a = (char*)(uintptr_t)0x10000;
+  int codes[] = {FA_OK, FA_ERR_NULL, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED_D, FA_ERR_ALIGNMENT,
+                 FA_ERR_HIP, FA_ERR_TILE};
+  size_t i, j;
+  fa_plan_info plan;
+
+  for (i = 0; i < sizeof codes / sizeof codes[0]; ++i) {
+    const char* s = fa_strerror(codes[i]);
+    CHECK(s != NULL && s[0] != '\0', "fa_strerror(%d) is empty", codes[i]);
+    for (j = 0; j < i; ++j) CHECK(strcmp(s, fa_strerror(codes[j])) != 0, "status strings repeat");
+  }
+  CHECK(fa_fwd(NULL, a + 0x10000, a + 0x20000, a + 0x30000, (float*)(a + 0x40000), 1, 1, 8, 64, 1,
+               0.125f, NULL) == FA_ERR_NULL, "NULL q accepted");
+  CHECK(fa_fwd(a, a + 0x10000, a + 0x20000, a + 0x30000, (float*)(a + 0x40000), 1, 1, 8, 96, 1,
+               0.125f, NULL) == FA_ERR_UNSUPPORTED_D, "d = 96 accepted");
+  CHECK(fa_fwd(a + 2, a + 0x10000, a + 0x20000, a + 0x30000, (float*)(a + 0x40000), 1, 1, 8, 64, 1,
+               0.125f, NULL) == FA_ERR_ALIGNMENT, "misaligned q accepted");
+  CHECK(fa_fwd(a, a + 0x10000, a + 0x20000, a + 0x30000, (float*)(a + 0x40000), 1, 1, 0, 64, 1,
+               0.125f, NULL) == FA_OK, "empty problem rejected");
+  CHECK(fa_fwd_plan(4, 12, 4096, 64, 1, 0, 0, 0, &plan) == FA_OK, "fa_fwd_plan failed");
+  CHECK(plan.block_m > 0 && plan.block_n > 0 && plan.waves > 0 && plan.grid > 0,
+        "fa_fwd_plan gave an empty launch");
+  printf("plan B4 H12 T4096 d64 causal: block %dx%d, %d waves, grid %lld, key split %d\n",
+         plan.block_m, plan.block_n, plan.waves, (long long)plan.grid, plan.key_split);
+  printf("ok\n");
+  return 0;
+}
+
+static int forward(int argc, char** argv) {
+  const char *in_path, *out_path;
+  int B, H, T, d, causal;
+  float scale;
+  size_t n, bytes_x, bytes_lse;
+  uint16_t *host_qkv, *host_o;
+  float* host_lse;
+  void *q, *k, *v, *o;
+  float* lse;
+  hipStream_t stream;
+  FILE* f;
+  int rc;
+
+  CHECK(argc == 10, "usage: c_consumer fwd IN OUT B H T d causal scale");
+  in_path = argv[2];
+  out_path = argv[3];
+  B = atoi(argv[4]);
+  H = atoi(argv[5]);
+  T = atoi(argv[6]);
+  d = atoi(argv[7]);
+  causal = atoi(argv[8]);
+  scale = (float)atof(argv[9]);
+  CHECK(B > 0 && H > 0 && T > 0 && d > 0, "sizes must be positive");
+  n = (size_t)B * H * T * d;
+  bytes_x = n * sizeof(uint16_t);
+  bytes_lse = (size_t)B * H * T * sizeof(float);
+
+  host_qkv = (uint16_t*)malloc(3 * bytes_x);
+  host_o = (uint16_t*)malloc(bytes_x);
+  host_lse = (float*)malloc(bytes_lse);
+  CHECK(host_qkv && host_o && host_lse, "out of host memory");
+  f = fopen(in_path, "rb");
+  CHECK(f != NULL, "cannot open %s", in_path);
+  CHECK(fread(host_qkv, 1, 3 * bytes_x, f) == 3 * bytes_x, "%s is shorter than q, k, v", in_path);
+  fclose(f);
+
+  HIP(hipMalloc(&q, bytes_x));
+  HIP(hipMalloc(&k, bytes_x));
+  HIP(hipMalloc(&v, bytes_x));
+  HIP(hipMalloc(&o, bytes_x));
+  HIP(hipMalloc((void**)&lse, bytes_lse));
+  HIP(hipStreamCreate(&stream));
+  HIP(hipMemcpy(q, host_qkv, bytes_x, hipMemcpyHostToDevice));
+  HIP(hipMemcpy(k, host_qkv + n, bytes_x, hipMemcpyHostToDevice));
+  HIP(hipMemcpy(v, host_qkv + 2 * n, bytes_x, hipMemcpyHostToDevice));
+
+  rc = fa_fwd(q, k, v, o, lse, B, H, T, d, causal, scale, (void*)stream);
+  CHECK(rc == FA_OK, "fa_fwd returned %d (%s)", rc, fa_strerror(rc));
+  HIP(hipStreamSynchronize(stream));
+  HIP(hipMemcpy(host_o, o, bytes_x, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(host_lse, lse, bytes_lse, hipMemcpyDeviceToHost));
+
+  f = fopen(out_path, "wb");
+  CHECK(f != NULL, "cannot open %s", out_path);
+  CHECK(fwrite(host_o, 1, bytes_x, f) == bytes_x && fwrite(host_lse, 1, bytes_lse, f) == bytes_lse,
+        "short write to %s", out_path);
+  CHECK(fclose(f) == 0, "cannot close %s", out_path);
+
+  HIP(hipStreamDestroy(stream));
+  HIP(hipFree(q));
+  HIP(hipFree(k));
+  HIP(hipFree(v));
+  HIP(hipFree(o));
+  HIP(hipFree(lse));
+  free(host_qkv);
+  free(host_o);
+  free(host_lse);
+  printf("ok\n");
+  return 0;
+}
+
+int main(int argc, char** argv) {
+  CHECK(argc >= 2, "usage: c_consumer host | fwd IN OUT B H T d causal scale");
+  if (strcmp(argv[1], "host") == 0) return host_checks();
+  if (strcmp(argv[1], "fwd") == 0) return forward(argc, argv);
+  CHECK(0, "unknown mode %s", argv[1]);
+  return 2;
+}

@@ -1,0 +1,82 @@
+"""libfa.so used from plain C (tests/c_consumer.c): the header compiles as strict C99, the library links
+into a C program, and that program's fa_fwd result agrees with the oracle.
+
+The C program is compiled with gcc into pytest's temporary directory (a fraction of a second); it
+runs as a child process, which allocates its own device memory through the HIP runtime's C API.
+"""
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_tiled_attention_07_amd import fa
+from exact_tiled_attention_07_amd.inputs import bf16_bits_to_f32, make_qkv
+
+from parity import assert_parity, compare
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+INCLUDE = os.path.join(ROOT, "include")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+pytestmark = pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not found")
+
+
+def gcc(*args):
+    r = subprocess.run(["gcc", *args], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return r
+
+
+def test_header_is_strict_c99(tmp_path):
+    src = tmp_path / "only_header.c"
+    src.write_text('#include "fa.h"\nint main(void) { return FA_OK; }\n')
+    gcc("-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", INCLUDE, str(src),
+        "-o", str(tmp_path / "only_header"))
+
+
+@pytest.fixture(scope="module")
+def consumer(tmp_path_factory):
+    lib_dir = os.path.dirname(fa.LIB_PATH)
+    assert os.path.exists(fa.LIB_PATH), f"{fa.LIB_PATH} is not built"
+    exe = str(tmp_path_factory.mktemp("c_consumer") / "c_consumer")
+    # -Wall -Wextra -Werror on the program; the HIP headers themselves are not held to -pedantic
+    gcc("-std=c99", "-O1", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+        "-I", INCLUDE, "-isystem", os.path.join(ROCM, "include"), os.path.join(HERE, "c_consumer.c"),
+        "-o", exe, "-L", lib_dir, "-lfa", "-L", os.path.join(ROCM, "lib"), "-lamdhip64",
+        f"-Wl,-rpath,{lib_dir}", f"-Wl,-rpath,{os.path.join(ROCM, 'lib')}")
+    return exe
+
+
+def test_c_program_host_checks(consumer):
+    r = subprocess.run([consumer, "host"], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert r.stdout.strip().endswith("ok")
+    assert "plan B4 H12 T4096 d64 causal: block 128x64, 4 waves, grid 1536, key split 1" in r.stdout
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("B,H,T,d,causal", [(1, 3, 200, 64, True), (2, 1, 77, 128, False)])
+def test_c_program_forward_matches_oracle(consumer, tmp_path, B, H, T, d, causal):
+    qb, kb, vb = make_qkv(B, H, T, d, seed=41 + T, sigma=1.5)
+    scale = float(np.float32(d ** -0.5))
+    inp, out = tmp_path / "qkv.bin", tmp_path / "o_lse.bin"
+    with open(inp, "wb") as f:
+        for x in (qb, kb, vb):
+            f.write(np.ascontiguousarray(x, dtype=np.uint16).tobytes())
+    print(f"[gpu] c_consumer fwd B{B} H{H} T{T} d{d} causal={causal}", flush=True)
+    r = subprocess.run([consumer, "fwd", str(inp), str(out), str(B), str(H), str(T), str(d),
+                        str(int(causal)), repr(scale)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    raw = out.read_bytes()
+    n = B * H * T * d
+    assert len(raw) == 2 * n + 4 * B * H * T
+    o = bf16_bits_to_f32(np.frombuffer(raw[:2 * n], dtype=np.uint16).reshape(B, H, T, d))
+    lse = np.frombuffer(raw[2 * n:], dtype=np.float32).reshape(B, H, T)
+    o_ref, lse_ref = oracle.attention_fwd(qb, kb, vb, causal, scale)
+    stats = compare(o, lse, o_ref, lse_ref)
+    print(f"[gpu] c_consumer {stats}", flush=True)
+    assert_parity(stats, "c_consumer")
