@@ -5,6 +5,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <tuple>
 
 #include "fa.h"
 #include "fa_bwd_kernel.hpp"
@@ -13,6 +14,23 @@
 #include "fa_merge_kernel.hpp"
 
 namespace {
+
+// Launches `fn` on `stream` with the given arguments (each converted to the kernel's parameter type)
+// and returns the status of this launch itself, not whatever error an earlier, unrelated HIP call
+// may have left for hipGetLastError.
+template <typename... P, typename... A>
+int launch_kernel(void (*fn)(P...), dim3 grid, dim3 block, void* stream, A... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "one argument per kernel parameter");
+  std::tuple<P...> vals(static_cast<P>(a)...);
+  void* ptrs[sizeof...(P)];
+  std::apply([&ptrs](P&... x) {
+    int i = 0;
+    ((ptrs[i++] = static_cast<void*>(&x)), ...);
+  }, vals);
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), grid, block, ptrs, 0,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
 
 using KernelFn = void (*)(const __bf16*, const __bf16*, const __bf16*, __bf16*, float*, int, int, int,
                           float, const uint8_t*, int, int, int, int, int);
@@ -115,11 +133,9 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
   const float scale_log2 = scale * fa::kLog2e;
   KernelFn fn = causal ? tile->causal_fn : tile->full_fn;
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * tile->waves), 0, (hipStream_t)stream,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, T, nq, BH,
-                     scale_log2, (const uint8_t*)nullptr, 0, 0, 0, 0, 0);
-  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  return FA_OK;
+  return launch_kernel(fn, dim3((unsigned)grid), dim3(64 * tile->waves), stream,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, T, nq, BH,
+                       scale_log2, (const uint8_t*)nullptr, 0, 0, 0, 0, 0);
 }
 
 // Block-sparse forward: the default tile shape (128 queries x 64 keys per tile, 4 waves) with the
@@ -161,11 +177,9 @@ int launch_sparse(const void* q, const void* k, const void* v, void* o, float* l
   KernelFn fn;
   if (d == 64) fn = causal ? &fa::fa_fwd_kernel<SparseFns<64>::Cc> : &fa::fa_fwd_kernel<SparseFns<64>::Cf>;
   else fn = causal ? &fa::fa_fwd_kernel<SparseFns<128>::Cc> : &fa::fa_fwd_kernel<SparseFns<128>::Cf>;
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, (const __bf16*)q,
-                     (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, T, nq, BH,
-                     scale * fa::kLog2e, (const uint8_t*)block_mask, mask_heads, 0, 0, 0, 0);
-  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  return FA_OK;
+  return launch_kernel(fn, dim3((unsigned)grid), dim3(256), stream, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, T, nq, BH,
+                       scale * fa::kLog2e, (const uint8_t*)block_mask, mask_heads, 0, 0, 0, 0);
 }
 
 // Partial forward over a key range: the default tile with the range selection and fp32 output.
@@ -221,11 +235,10 @@ int launch_ranges(const void* q, const void* k, const void* v, float* o_part, fl
   else
     fn = few ? (causal ? &fa::fa_fwd_kernel<RangeFns<128>::CcFew> : &fa::fa_fwd_kernel<RangeFns<128>::CfFew>)
              : (causal ? &fa::fa_fwd_kernel<RangeFns<128>::Cc> : &fa::fa_fwd_kernel<RangeFns<128>::Cf>);
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid, (unsigned)n_splits), dim3(256), 0, (hipStream_t)stream,
-                     (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o_part, lse_part, T,
-                     nq, BH, scale * fa::kLog2e, (const uint8_t*)nullptr, 0, k_begin, k_end, Tk, k_chunk);
-  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  return FA_OK;
+  return launch_kernel(fn, dim3((unsigned)grid, (unsigned)n_splits), dim3(256), stream,
+                       (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o_part,
+                       lse_part, T, nq, BH, scale * fa::kLog2e, (const uint8_t*)nullptr, 0, k_begin,
+                       k_end, Tk, k_chunk);
 }
 
 int launch_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part, int B,
@@ -281,10 +294,8 @@ int launch_merge_kernel(const float* o_parts, const float* lse_parts, int n_part
   const int64_t grid = (rows + rpb - 1) / rpb;
   if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
   auto fn = d == 64 ? &fa::fa_merge_kernel<64> : &fa::fa_merge_kernel<128>;
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, o_parts, lse_parts,
-                     n_parts, (__bf16*)o, lse, rows);
-  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  return FA_OK;
+  return launch_kernel(fn, dim3((unsigned)grid), dim3(256), stream, o_parts, lse_parts,
+                       n_parts, (__bf16*)o, lse, rows);
 }
 
 int launch_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
@@ -352,11 +363,9 @@ int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   else
     fn = causal ? &fa::fa_fwd_fp8_kernel<fa::Fp8Cfg<128, true>> : &fa::fa_fwd_fp8_kernel<fa::Fp8Cfg<128, false>>;
   static_assert(fa::Fp8Cfg<64, true>::BM == 128 && fa::Fp8Cfg<128, true>::BM == 128, "Q block");
-  hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, (const uint8_t*)q,
-                     (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse, T, nq, BH, (float)sl2,
-                     v_descale);
-  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  return FA_OK;
+  return launch_kernel(fn, dim3((unsigned)grid), dim3(256), stream, (const uint8_t*)q,
+                       (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse, T, nq, BH, (float)sl2,
+                       v_descale);
 }
 
 template <int D>
@@ -407,18 +416,15 @@ int launch_bwd_kernels(const void* q, const void* k, const void* v, const void* 
   const int64_t grid = (int64_t)nb * BH;
   if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
   const float scale_log2 = scale * fa::kLog2e;
-  hipStream_t s = (hipStream_t)stream;
   auto dq_fn = causal ? &fa::fa_bwd_dq_kernel<Cc> : &fa::fa_bwd_dq_kernel<Cf>;
   auto dkdv_fn = causal ? &fa::fa_bwd_dkdv_kernel<Cc> : &fa::fa_bwd_dkdv_kernel<Cf>;
-  hipLaunchKernelGGL(dq_fn, dim3((unsigned)grid), dim3(Cc::THREADS), 0, s, (const __bf16*)q,
-                     (const __bf16*)k, (const __bf16*)v, (const __bf16*)o, lse, (const __bf16*)dout,
-                     (__bf16*)dq, delta, T, nb, BH, scale, scale_log2);
-  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  hipLaunchKernelGGL(dkdv_fn, dim3((unsigned)grid), dim3(Cc::THREADS), 0, s, (const __bf16*)q,
-                     (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dout,
-                     (const float*)delta, (__bf16*)dk, (__bf16*)dv, T, nb, BH, scale, scale_log2);
-  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  return FA_OK;
+  const int rc = launch_kernel(dq_fn, dim3((unsigned)grid), dim3(Cc::THREADS), stream, (const __bf16*)q,
+                               (const __bf16*)k, (const __bf16*)v, (const __bf16*)o, lse,
+                               (const __bf16*)dout, (__bf16*)dq, delta, T, nb, BH, scale, scale_log2);
+  if (rc != FA_OK) return rc;
+  return launch_kernel(dkdv_fn, dim3((unsigned)grid), dim3(Cc::THREADS), stream, (const __bf16*)q,
+                       (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dout,
+                       (const float*)delta, (__bf16*)dk, (__bf16*)dv, T, nb, BH, scale, scale_log2);
 }
 
 }  // namespace
@@ -439,14 +445,16 @@ int fa_fwd_partial(const void* q, const void* k, const void* v, float* o_part, f
 }
 
 size_t fa_splitkv_workspace_bytes(int B, int H, int T, int d, int n_splits) {
-  if (B < 0 || H < 0 || T < 0 || d < 0 || n_splits < 1) return 0;
-  const size_t per_part = (size_t)B * H * T * ((size_t)d + 1) * 4;  // B*H*T <= 2^46: no overflow
+  if (check_sizes(B, H, T, d) != FA_OK || n_splits < 1 || n_splits > FA_MERGE_MAX_PARTS) return 0;
+  // B*H*T <= 2^46 and d + 1 <= 129: one part is below 2^56 bytes
+  const size_t per_part = (size_t)B * H * T * ((size_t)d + 1) * 4;
   if (per_part > SIZE_MAX / (size_t)n_splits) return 0;
   return (size_t)n_splits * per_part;
 }
 
 int fa_splitkv_splits(int B, int H, int T, int Tk, int d) {
-  if (B <= 0 || H <= 0 || T <= 0 || Tk <= 0 || (d != 64 && d != 128)) return 1;
+  if (B <= 0 || H <= 0 || T <= 0 || Tk <= 0 || check_sizes(B, H, T, d) != FA_OK || Tk > FA_MAX_T)
+    return 1;
   // as many workgroups as two per compute unit hold at once (not more: a second round would wait
   // for the first), with at least 8 key tiles (512 keys) per range
   const int64_t base = (int64_t)((T + 127) / 128) * B * H;

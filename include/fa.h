@@ -46,7 +46,8 @@ typedef enum fa_status {
   FA_ERR_INVALID_ARG = -2,    /* negative size, size too large, scale not finite and > 0, overlap */
   FA_ERR_UNSUPPORTED_D = -3,  /* head dim d is not 64 or 128 */
   FA_ERR_ALIGNMENT = -4,      /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
-  FA_ERR_HIP = -5,            /* the HIP runtime reported an error at launch */
+  FA_ERR_HIP = -5,            /* the kernel launch itself failed (its own status, not an earlier
+                                 error still pending in hipGetLastError) */
   FA_ERR_TILE = -6            /* fa_fwd_ex / fa_fwd_plan: tile shape not in the supported table */
 } fa_status;
 
@@ -189,8 +190,14 @@ int fa_merge(const float* o_parts, const float* lse_parts, int n_parts, void* o,
  *              overwritten
  * Two kernels run in order on `stream`. No allocation. Returns FA_OK or a negative fa_status.
  */
-size_t fa_splitkv_workspace_bytes(int B, int H, int T, int d, int n_splits); /* 0 if invalid */
-int fa_splitkv_splits(int B, int H, int T, int Tk, int d); /* a split count that fills the GPU */
+/* Workspace bytes fa_fwd_splitkv needs: n_splits * B*H*T * (d + 1) * 4 (fp32 O and LSE per range).
+ * 0 for an empty problem, or when fa_fwd_splitkv would reject the sizes (B, H, T or d out of range,
+ * n_splits outside 1 .. FA_MERGE_MAX_PARTS) or the product does not fit in size_t. Host-only. */
+size_t fa_splitkv_workspace_bytes(int B, int H, int T, int d, int n_splits);
+/* A split count for these sizes that fills the GPU: enough key ranges for about 512 workgroups, each
+ * range at least 8 tiles of 64 keys, at most FA_MERGE_MAX_PARTS. 1 for empty or out-of-range sizes.
+ * Host-only. */
+int fa_splitkv_splits(int B, int H, int T, int Tk, int d);
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                    int T, int Tk, int d, int causal, float scale, int n_splits, void* workspace,
                    size_t workspace_bytes, void* stream);

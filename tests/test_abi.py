@@ -251,6 +251,15 @@ def test_splitkv_checks():
     assert lib.fa_splitkv_workspace_bytes(2, 3, 5, 64, 4) == 4 * 2 * 3 * 5 * 65 * 4
     assert lib.fa_splitkv_workspace_bytes(2, 3, 5, 64, 0) == 0
     assert lib.fa_splitkv_workspace_bytes(-1, 3, 5, 64, 1) == 0
+    # sizes fa_fwd_splitkv rejects give 0, never a wrapped product
+    assert lib.fa_splitkv_workspace_bytes(2, 3, 5, 96, 1) == 0
+    assert lib.fa_splitkv_workspace_bytes(2, 3, 5, 64, 4097) == 0
+    assert lib.fa_splitkv_workspace_bytes(1, 1, (1 << 22) + 1, 64, 1) == 0
+    assert lib.fa_splitkv_workspace_bytes(1 << 13, 1 << 12, 1, 64, 1) == 0
+    assert lib.fa_splitkv_workspace_bytes(1 << 30, 1 << 30, 1 << 30, 64, 1) == 0
+    # the largest accepted sizes: one part fits, 4096 of them (65 * 2^60 bytes) do not
+    assert lib.fa_splitkv_workspace_bytes(1 << 12, 1 << 12, 1 << 22, 64, 1) == (1 << 46) * 65 * 4
+    assert lib.fa_splitkv_workspace_bytes(1 << 12, 1 << 12, 1 << 22, 64, 4096) == 0
     assert call_splitkv(T=0) == fa.FA_OK
     assert call_splitkv(ws=None) == fa.FA_ERR_NULL
     assert call_splitkv(n=0) == fa.FA_ERR_INVALID_ARG
@@ -271,6 +280,10 @@ def test_splitkv_split_count():
     assert lib.fa_splitkv_splits(4, 12, 4096, 4096, 64) == 1
     assert lib.fa_splitkv_splits(1, 1, 1, 100, 64) == 1
     assert lib.fa_splitkv_splits(0, 1, 1, 100, 64) == 1
+    # out-of-range sizes (no overflow in the tile counts)
+    assert lib.fa_splitkv_splits(1, 1, 2 ** 31 - 1, 100, 64) == 1
+    assert lib.fa_splitkv_splits(1, 1, 1, 2 ** 31 - 1, 64) == 1
+    assert lib.fa_splitkv_splits(1, 1, 1, 65536, 96) == 1
 
 
 def call_merge(n=2, B=1, H=1, T=8, d=64, **kw):

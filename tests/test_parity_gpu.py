@@ -256,6 +256,33 @@ def test_side_stream():
     assert_parity(compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref), "side stream")
 
 
+def test_earlier_hip_error_does_not_fail_a_good_launch():
+    """A failed HIP call made before fa_fwd (here hipSetDevice on a device that does not exist, an
+    error the runtime reports on the host) must not turn a good launch into FA_ERR_HIP: the status
+    is that of the launch itself. The C entry point is called directly, with no torch call between
+    the failed call and the launch. hipSetDevice and hipGetLastError are looked up through libfa.so,
+    so they belong to the HIP runtime the library itself uses."""
+    import ctypes
+    from exact_tiled_attention_07_amd import fa as binding
+    lib = binding.lib()
+    set_device, last_error = lib.hipSetDevice, lib.hipGetLastError
+    set_device.argtypes, set_device.restype, last_error.restype = [ctypes.c_int], ctypes.c_int, ctypes.c_int
+    qb, kb, vb = make_qkv(1, 2, 300, 64, seed=53)
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    o = torch.empty_like(q)
+    lse = torch.empty(1, 2, 300, dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    last_error()
+    assert set_device(1 << 20) != 0
+    rc = lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), 1, 2, 300, 64,
+                    1, 0.125, None)
+    last_error()  # leave no error behind for the rest of the process
+    assert rc == binding.FA_OK, lib.fa_strerror(rc)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_fwd(qb, kb, vb, True, 0.125)
+    assert_parity(compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref), "after a HIP error")
+
+
 def test_binding_rejects_bad_tensors():
     q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(TypeError):
