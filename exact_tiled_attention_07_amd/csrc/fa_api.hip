@@ -32,6 +32,25 @@ int launch_kernel(void (*fn)(P...), dim3 grid, dim3 block, void* stream, A... a)
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// Grid of n workgroups of `threads` work-items (times `splits` in y). The dispatch counts
+// work-items per dimension in 32 bits, so above (2^32 - 1) / threads workgroups the 1-D grid is
+// folded into x (a multiple of 8) and z; the kernels recover the flat index and let the workgroups
+// past n exit. FA_ERR_INVALID_ARG when even the folded grid does not fit (n >= 2^31, or z > 65535).
+int fold_grid(int64_t n, int threads, int splits, dim3* grid) {
+  const int64_t max_x = (int64_t)UINT32_MAX / threads;
+  if (n <= 0 || n > INT32_MAX || splits < 1 || splits > 65535) return FA_ERR_INVALID_ARG;
+  if (n <= max_x) {
+    *grid = dim3((unsigned)n, (unsigned)splits, 1u);
+    return FA_OK;
+  }
+  const int64_t max_x8 = max_x & ~(int64_t)7;
+  const int64_t z = (n + max_x8 - 1) / max_x8;
+  const int64_t x = ((n + z - 1) / z + 7) & ~(int64_t)7;  // <= max_x8; fewer than 8 * z spare
+  if (z > 65535) return FA_ERR_INVALID_ARG;
+  *grid = dim3((unsigned)x, (unsigned)splits, (unsigned)z);
+  return FA_OK;
+}
+
 using KernelFn = void (*)(const __bf16*, const __bf16*, const __bf16*, __bf16*, float*, int, int, int,
                           float, const uint8_t*, int, int, int, int, int);
 
@@ -129,11 +148,11 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
 
   const int nq = (T + tile->block_m - 1) / tile->block_m;
   const int BH = B * H;
-  const int64_t grid = (int64_t)nq * BH;
-  if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  dim3 grid;
+  if (fold_grid((int64_t)nq * BH, 64 * tile->waves, 1, &grid) != FA_OK) return FA_ERR_INVALID_ARG;
   const float scale_log2 = scale * fa::kLog2e;
   KernelFn fn = causal ? tile->causal_fn : tile->full_fn;
-  return launch_kernel(fn, dim3((unsigned)grid), dim3(64 * tile->waves), stream,
+  return launch_kernel(fn, grid, dim3(64 * tile->waves), stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, T, nq, BH,
                        scale_log2, (const uint8_t*)nullptr, 0, 0, 0, 0, 0);
 }
@@ -172,12 +191,12 @@ int launch_sparse(const void* q, const void* k, const void* v, void* o, float* l
   if (overlaps(o, bytes, lse, lse_bytes)) return FA_ERR_INVALID_ARG;
   if (n_elem == 0) return FA_OK;
   const int BH = B * H;
-  const int64_t grid = (int64_t)nq * BH;
-  if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  dim3 grid;
+  if (fold_grid((int64_t)nq * BH, 256, 1, &grid) != FA_OK) return FA_ERR_INVALID_ARG;
   KernelFn fn;
   if (d == 64) fn = causal ? &fa::fa_fwd_kernel<SparseFns<64>::Cc> : &fa::fa_fwd_kernel<SparseFns<64>::Cf>;
   else fn = causal ? &fa::fa_fwd_kernel<SparseFns<128>::Cc> : &fa::fa_fwd_kernel<SparseFns<128>::Cf>;
-  return launch_kernel(fn, dim3((unsigned)grid), dim3(256), stream, (const __bf16*)q,
+  return launch_kernel(fn, grid, dim3(256), stream, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, T, nq, BH,
                        scale * fa::kLog2e, (const uint8_t*)block_mask, mask_heads, 0, 0, 0, 0);
 }
@@ -225,8 +244,8 @@ int launch_ranges(const void* q, const void* k, const void* v, float* o_part, fl
                   int k_chunk, int n_splits, void* stream) {
   const int nq = (T + 127) / 128;
   const int BH = B * H;
-  const int64_t grid = (int64_t)nq * BH;
-  if (grid > 0x7fffffffLL || n_splits > 65535) return FA_ERR_INVALID_ARG;
+  dim3 grid;
+  if (fold_grid((int64_t)nq * BH, 256, n_splits, &grid) != FA_OK) return FA_ERR_INVALID_ARG;
   const bool few = T < RangeFns<64>::Cc::BM;
   KernelFn fn;
   if (d == 64)
@@ -235,7 +254,7 @@ int launch_ranges(const void* q, const void* k, const void* v, float* o_part, fl
   else
     fn = few ? (causal ? &fa::fa_fwd_kernel<RangeFns<128>::CcFew> : &fa::fa_fwd_kernel<RangeFns<128>::CfFew>)
              : (causal ? &fa::fa_fwd_kernel<RangeFns<128>::Cc> : &fa::fa_fwd_kernel<RangeFns<128>::Cf>);
-  return launch_kernel(fn, dim3((unsigned)grid, (unsigned)n_splits), dim3(256), stream,
+  return launch_kernel(fn, grid, dim3(256), stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o_part,
                        lse_part, T, nq, BH, scale * fa::kLog2e, (const uint8_t*)nullptr, 0, k_begin,
                        k_end, Tk, k_chunk);
@@ -291,10 +310,10 @@ int launch_merge(const float* o_parts, const float* lse_parts, int n_parts, void
 int launch_merge_kernel(const float* o_parts, const float* lse_parts, int n_parts, void* o, float* lse,
                         int64_t rows, int d, void* stream) {
   const int rpb = 256 / (d / 4);
-  const int64_t grid = (rows + rpb - 1) / rpb;
-  if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  dim3 grid;
+  if (fold_grid((rows + rpb - 1) / rpb, 256, 1, &grid) != FA_OK) return FA_ERR_INVALID_ARG;
   auto fn = d == 64 ? &fa::fa_merge_kernel<64> : &fa::fa_merge_kernel<128>;
-  return launch_kernel(fn, dim3((unsigned)grid), dim3(256), stream, o_parts, lse_parts,
+  return launch_kernel(fn, grid, dim3(256), stream, o_parts, lse_parts,
                        n_parts, (__bf16*)o, lse, rows);
 }
 
@@ -353,8 +372,8 @@ int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   if (n_elem == 0) return FA_OK;
   const int nq = (T + 127) / 128;
   const int BH = B * H;
-  const int64_t grid = (int64_t)nq * BH;
-  if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  dim3 grid;
+  if (fold_grid((int64_t)nq * BH, 256, 1, &grid) != FA_OK) return FA_ERR_INVALID_ARG;
   using Fn8 = void (*)(const uint8_t*, const uint8_t*, const uint8_t*, __bf16*, float*, int, int, int,
                        float, float);
   Fn8 fn;
@@ -363,7 +382,7 @@ int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   else
     fn = causal ? &fa::fa_fwd_fp8_kernel<fa::Fp8Cfg<128, true>> : &fa::fa_fwd_fp8_kernel<fa::Fp8Cfg<128, false>>;
   static_assert(fa::Fp8Cfg<64, true>::BM == 128 && fa::Fp8Cfg<128, true>::BM == 128, "Q block");
-  return launch_kernel(fn, dim3((unsigned)grid), dim3(256), stream, (const uint8_t*)q,
+  return launch_kernel(fn, grid, dim3(256), stream, (const uint8_t*)q,
                        (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse, T, nq, BH, (float)sl2,
                        v_descale);
 }
@@ -413,16 +432,16 @@ int launch_bwd_kernels(const void* q, const void* k, const void* v, const void* 
   using Cf = fa::BwdCfg<D, false>;
   const int nb = (T + Cc::BM - 1) / Cc::BM;  // query blocks (dQ kernel) = key blocks (dK/dV kernel)
   const int BH = B * H;
-  const int64_t grid = (int64_t)nb * BH;
-  if (grid > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  dim3 grid;
+  if (fold_grid((int64_t)nb * BH, Cc::THREADS, 1, &grid) != FA_OK) return FA_ERR_INVALID_ARG;
   const float scale_log2 = scale * fa::kLog2e;
   auto dq_fn = causal ? &fa::fa_bwd_dq_kernel<Cc> : &fa::fa_bwd_dq_kernel<Cf>;
   auto dkdv_fn = causal ? &fa::fa_bwd_dkdv_kernel<Cc> : &fa::fa_bwd_dkdv_kernel<Cf>;
-  const int rc = launch_kernel(dq_fn, dim3((unsigned)grid), dim3(Cc::THREADS), stream, (const __bf16*)q,
+  const int rc = launch_kernel(dq_fn, grid, dim3(Cc::THREADS), stream, (const __bf16*)q,
                                (const __bf16*)k, (const __bf16*)v, (const __bf16*)o, lse,
                                (const __bf16*)dout, (__bf16*)dq, delta, T, nb, BH, scale, scale_log2);
   if (rc != FA_OK) return rc;
-  return launch_kernel(dkdv_fn, dim3((unsigned)grid), dim3(Cc::THREADS), stream, (const __bf16*)q,
+  return launch_kernel(dkdv_fn, grid, dim3(Cc::THREADS), stream, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dout,
                        (const float*)delta, (__bf16*)dk, (__bf16*)dv, T, nb, BH, scale, scale_log2);
 }

@@ -213,6 +213,14 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 // Map the flat workgroup id to (Q block, batch*head). Workgroups are handed to the 8 XCDs round
 // robin, so when B*H is a multiple of 8 each XCD gets its own set of heads (their K/V stay in that
 // XCD's L2), and within an XCD the Q blocks with the most K/V tiles start first.
+// Flat index of this workgroup among n. The dispatch counts work-items per grid dimension in 32
+// bits, so a launch of more workgroups than one dimension holds folds them into x (a multiple of
+// 8, which keeps the XCD round robin of the flat index) and z; workgroups past n get -1 and exit.
+__device__ __forceinline__ int block_index(int64_t n) {
+  const int64_t b = (int64_t)blockIdx.z * gridDim.x + blockIdx.x;
+  return b < n ? (int)b : -1;
+}
+
 template <bool CAUSAL>
 __device__ __forceinline__ void map_block(int bid, int nq, int BH, int& qblk, int& bh) {
   int rank;
@@ -251,8 +259,10 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   (void)t_keys;
   (void)k_chunk;
 
+  const int bid = block_index((int64_t)nq * BH);
+  if (bid < 0) return;
   int qblk, bh;
-  map_block<C::CAUSAL>(blockIdx.x, nq, BH, qblk, bh);
+  map_block<C::CAUSAL>(bid, nq, BH, qblk, bh);
   const int q0 = qblk * BM;
   // T is the number of queries. A key range may come from a longer sequence of Tk keys (queries
   // then sit at its end: query i is at key position i + coff, the causal diagonal shifted by coff),
@@ -456,7 +466,8 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   // Per query row: the exact running max m (base 2, scaled; the same in both halves of the wave),
   // the fp32 sum l of this lane's half of the exponentials, and the factor alpha = exp2(m_old -
   // m_new) still to be applied to acc and l before the next block is added. Because m is the
-  // exact max, the largest weight of a row is exactly 1 and needs no rounding in bf16.
+  // exact max, the largest weight of a row rounds to exactly 1 in bf16 (in fp32 it is exp2 of the
+  // rounding residual of m, which the FMA s * c - m keeps: within 2^-23 of 1).
   f32x16 acc[CB][QB];
   float m_run[QB], l_run[QB], alpha[QB];
 #pragma unroll

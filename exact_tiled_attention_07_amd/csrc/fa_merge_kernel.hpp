@@ -23,7 +23,8 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
   constexpr int TPR = D / 4;
   constexpr int RPB = 256 / TPR;
   constexpr int U = 4;  // parts per batch of loads
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  // a long grid is folded into x and z (32-bit work-item counts per dimension)
+  const int64_t row = ((int64_t)blockIdx.z * gridDim.x + blockIdx.x) * RPB + threadIdx.x / TPR;
   const int c4 = threadIdx.x % TPR;
   if (row >= rows) return;
   const float* lp = lse_parts + row;

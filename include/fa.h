@@ -95,7 +95,9 @@ typedef struct fa_plan_info {
   int block_n;     /* keys per K/V tile */
   int waves;       /* wavefronts per workgroup */
   int q_blocks;    /* ceil(T / block_m) */
-  long long grid;  /* workgroups launched: q_blocks * B * H (one per (Q block, batch*head)) */
+  long long grid;  /* workgroups: q_blocks * B * H (one per (Q block, batch*head)); a grid of more
+                      than (2^32 - 1) / (64 * waves) workgroups is launched folded into two grid
+                      dimensions, with fewer than 8 spare workgroups per fold that exit at once */
   int lds_bytes;   /* LDS per workgroup: double-buffered K and V tiles */
   long long kv_tiles; /* K/V tiles processed by all workgroups (fully masked ones skipped) */
   int key_split;   /* 1, or 2: two waves share each 32-query block, each taking every other K/V tile,

@@ -112,6 +112,36 @@ def test_one_head_very_long_sequence():
     assert_parity(stats, f"T={T}")
 
 
+FA_MAX_T = 1 << 22  # include/fa.h: the largest accepted sequence length
+
+
+def gpu_rows(o, lse, rows):
+    """The sampled rows of a GPU result, copied to the host (not the whole, multi-GiB output)."""
+    idx = torch.as_tensor(rows, dtype=torch.int64, device=o.device)
+    return (o.reshape(-1, o.shape[-1]).index_select(0, idx).float().cpu().numpy(),
+            lse.reshape(-1).index_select(0, idx).cpu().numpy())
+
+
+@pytest.mark.parametrize("T,d", [(FA_MAX_T, 64), (FA_MAX_T - 1, 128)])
+def test_longest_sequence(T, d):
+    # one head at the largest accepted length (and one short of it at d = 128, a ragged last tile):
+    # 32768 Q blocks, the last walking 65536 K/V tiles; byte offsets up to 2^30 per tensor; sampled rows
+    B, H = 1, 1
+    qb, kb, vb = make_qkv(B, H, T, d, seed=T % 1000 + d, sigma=1.5)
+    say(f"[gpu] longest sequence T={T} d={d}")
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    scale = d ** -0.5
+    o, lse = fa.fwd(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    del q, k, v
+    rows = sample_rows(B, H, T, 40, seed=d)
+    o_s, lse_s = gpu_rows(o, lse, rows)
+    o_ref, lse_ref = oracle.attention_rows(qb, kb, vb, True, scale, rows)
+    stats = compare(o_s, lse_s, o_ref, lse_ref)
+    say(f"[gpu] T={T} d={d} {stats}")
+    assert_parity(stats, f"T={T} d={d}")
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_key_split_long_sequence(causal):
     # two heads of T = 12289: the default launch is the key split (97 x 2 workgroups of 128 queries
