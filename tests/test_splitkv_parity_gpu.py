@@ -191,6 +191,33 @@ def test_splitkv_against_oracle(B, H, T, Tk, d, n, causal):
     check_against_cross(o, lse, oracle.attention_fwd_cross(qb, kb, vb, causal, scale), f"splitkv n={used}")
 
 
+@pytest.mark.parametrize("T,Tk,d", [(16, 1 << 22, 64), (1, (1 << 22) - 1, 128)])
+def test_splitkv_longest_keys(T, Tk, d):
+    # the largest accepted key length (FA_MAX_T = 2^22; one short of it at d = 128, a ragged last
+    # tile) with the split count the library picks: 512 ranges of 8192 keys, merged in log space
+    B, H = 1, 1
+    qb, kb, vb = cross_inputs(B, H, T, Tk, d, seed=8000 + d)
+    scale = 1.0 / math.sqrt(d)
+    used = fa.splitkv_splits(B, H, T, Tk, d)
+    say(f"[gpu splitkv] longest keys T={T} Tk={Tk} d={d} n_splits={used}")
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    o, lse = fa.fwd_splitkv(q, k, v, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    check_against_cross(o, lse, oracle.attention_fwd_cross(qb, kb, vb, True, scale), f"Tk={Tk} n={used}")
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_splitkv_most_parts(causal):
+    # FA_MERGE_MAX_PARTS = 4096 key ranges of one 64-key tile each, all merged by one fa_merge launch
+    B, H, T, Tk, d = 1, 2, 16, 4096 * 64, 64
+    qb, kb, vb = cross_inputs(B, H, T, Tk, d, seed=8100)
+    say(f"[gpu splitkv] most parts T={T} Tk={Tk} n_splits=4096 causal={causal}")
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    o, lse = fa.fwd_splitkv(q, k, v, causal=causal, scale=0.125, n_splits=4096)
+    torch.cuda.synchronize()
+    check_against_cross(o, lse, oracle.attention_fwd_cross(qb, kb, vb, causal, 0.125), "4096 parts")
+
+
 def test_splitkv_decode_workload_sampled():
     # decoding 16 queries against the 16384-key sequences of the B=4, H=12, d=64 workload, with the
     # split count the library picks; every head is checked (the oracle handles 16 rows per head)
