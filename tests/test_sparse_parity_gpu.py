@@ -96,6 +96,21 @@ def test_sparse_long_sequence():
     check(qb, kb, vb, mask, True, 0.125, "T=16384")
 
 
+def test_sparse_longest_sequence_full_tile_list():
+    # FA_SPARSE_MAX_T = 65536, non-causal: 5% of the blocks plus the diagonal ones, and the first and
+    # last query blocks with every key block set, so their tile lists hold the 1024 tiles a list
+    # can take (T / 64); one head
+    T = 65536
+    qb, kb, vb = make_qkv(1, 1, T, 64, seed=31)
+    mask = random_mask(T, 1, 0.05, 9)
+    for i in range(mask.shape[1]):
+        mask[0, i, 2 * i:2 * i + 2] = 1
+    mask[0, 0, :] = 1
+    mask[0, -1, :] = 1
+    assert mask.shape == (1, 512, 1024)
+    check(qb, kb, vb, mask, False, 0.125, "T=65536 full lists")
+
+
 def test_sparse_binding_rejects():
     q = torch.zeros(1, 1, 100, 64, dtype=torch.bfloat16, device=DEV)
     with pytest.raises(ValueError):
