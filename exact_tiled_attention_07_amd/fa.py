@@ -39,6 +39,18 @@ class PlanInfo(ctypes.Structure):
                 ("lds_bytes", ctypes.c_int), ("kv_tiles", ctypes.c_longlong), ("key_split", ctypes.c_int)]
 
 
+class _Int(ctypes.c_int):
+    """A C ``int`` argument that refuses values outside its range (plain ctypes would wrap them
+    silently, e.g. 2**32 + 5 to 5)."""
+
+    @classmethod
+    def from_param(cls, value):
+        v = int(value)
+        if not -(1 << 31) <= v < (1 << 31):
+            raise OverflowError(f"{value} does not fit in a C int")
+        return ctypes.c_int(v)
+
+
 def lib():
     """Load libfa.so (once). Raises if it has not been built."""
     global _lib
@@ -48,29 +60,29 @@ def lib():
         raise FileNotFoundError(
             f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
     L = ctypes.CDLL(LIB_PATH)
-    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    vp, i, f = ctypes.c_void_p, _Int, ctypes.c_float
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
-    L.fa_fwd.restype = i
+    L.fa_fwd.restype = ctypes.c_int
     L.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, i, i]
-    L.fa_fwd_ex.restype = i
+    L.fa_fwd_ex.restype = ctypes.c_int
     L.fa_fwd_plan.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(PlanInfo)]
-    L.fa_fwd_plan.restype = i
+    L.fa_fwd_plan.restype = ctypes.c_int
     L.fa_fwd_sparse.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp, i, vp]
-    L.fa_fwd_sparse.restype = i
+    L.fa_fwd_sparse.restype = ctypes.c_int
     L.fa_fwd_partial.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, vp]
-    L.fa_fwd_partial.restype = i
+    L.fa_fwd_partial.restype = ctypes.c_int
     L.fa_merge.argtypes = [vp, vp, i, vp, vp, i, i, i, i, vp]
-    L.fa_merge.restype = i
+    L.fa_merge.restype = ctypes.c_int
     L.fa_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
     L.fa_splitkv_workspace_bytes.restype = ctypes.c_size_t
     L.fa_splitkv_splits.argtypes = [i, i, i, i, i]
-    L.fa_splitkv_splits.restype = i
+    L.fa_splitkv_splits.restype = ctypes.c_int
     L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t, vp]
-    L.fa_fwd_splitkv.restype = i
+    L.fa_fwd_splitkv.restype = ctypes.c_int
     L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, f, f, f, vp]
-    L.fa_fwd_fp8.restype = i
+    L.fa_fwd_fp8.restype = ctypes.c_int
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
-    L.fa_bwd.restype = i
+    L.fa_bwd.restype = ctypes.c_int
     L.fa_strerror.argtypes = [i]
     L.fa_strerror.restype = ctypes.c_char_p
     _lib = L

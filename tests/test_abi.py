@@ -29,6 +29,17 @@ def test_library_exports_every_declared_function():
         assert hasattr(lib, n)
 
 
+def test_int_arguments_out_of_c_range_raise():
+    # ctypes would wrap 2**32 + 8 to 8 (a valid size) without this check in the binding
+    import ctypes
+    for kw in ("B", "H", "T"):
+        with pytest.raises(ctypes.ArgumentError):
+            call(**{kw: (1 << 32) + 8})
+    with pytest.raises(ctypes.ArgumentError):
+        fa.lib().fa_splitkv_workspace_bytes(1, 1, 8, 64, -(1 << 31) - 1)
+    assert call(T=(1 << 31) - 1) == fa.FA_ERR_INVALID_ARG  # in range: the library's own check
+
+
 def test_null_pointers():
     for kw in ("q", "k", "v", "o", "lse"):
         assert call(**{kw: None}) == fa.FA_ERR_NULL
