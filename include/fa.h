@@ -27,6 +27,8 @@
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default stream). They return
  *     after enqueueing the kernel and never synchronise. The library keeps no mutable global state
  *     and is safe to call from several host threads.
+ *   - A call enqueues kernel launches only (no allocation, memset, copy or synchronisation), so it
+ *     may be captured into a HIP graph on a capturing stream and replayed.
  *   - Arguments are checked before anything is launched; on any error nothing is written.
  *   - B*H*T == 0 is a valid empty problem: FA_OK, nothing launched, nothing written.
  *   - Inputs must be finite. NaN or Inf inputs give unspecified outputs (no error is raised).

@@ -1,0 +1,125 @@
+"""The entry points inside a captured HIP graph (torch.cuda.graph over the C-ABI calls).
+
+The library launches kernels only: no allocation, no memset, no synchronisation, so a call can be
+captured on the capture stream and replayed. Each test captures once with static buffers, then
+replays several times; between replays the inputs are overwritten by eager copies and the program
+synchronises, and every replay must equal an eager call on the same inputs bit for bit (every
+launch here is deterministic).
+"""
+import pytest
+import torch
+
+import exact_tiled_attention_07_amd as fa
+from exact_tiled_attention_07_amd.inputs import make_qkv, to_torch_bf16
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+REPLAYS = 4
+
+
+def capture(fn):
+    """Warm fn up on a side stream, then capture it into a graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def assert_same(a, b, label):
+    assert torch.equal(bits(a), bits(b)), label
+
+
+def fill(dst_tensors, B, H, T, d, seed):
+    for dst, src in zip(dst_tensors, make_qkv(B, H, T, d, seed=seed)):
+        dst.copy_(to_torch_bf16(src, DEV))
+
+
+@pytest.mark.parametrize("B,H,T,d,causal", [(2, 3, 1000, 64, True), (1, 2, 300, 128, False),
+                                            (1, 2, 40, 64, True)])
+def test_fwd_graph_replays(B, H, T, d, causal):
+    # the last shape takes the key-split launch
+    q, k, v = (torch.empty(B, H, T, d, dtype=torch.bfloat16, device=DEV) for _ in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, T, dtype=torch.float32, device=DEV)
+    fill((q, k, v), B, H, T, d, seed=1)
+    g = capture(lambda: fa.fwd(q, k, v, causal=causal, out=o, lse=lse))
+    for r in range(REPLAYS):
+        fill((q, k, v), B, H, T, d, seed=100 + r)
+        o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        o_e, lse_e = fa.fwd(q, k, v, causal=causal)
+        torch.cuda.synchronize()
+        assert_same(o, o_e, f"o, replay {r}")
+        assert_same(lse, lse_e, f"lse, replay {r}")
+
+
+def test_splitkv_graph_replays():
+    # two kernels (key ranges, then the merge) and a caller-owned workspace
+    B, H, T, Tk, d = 2, 3, 4, 5000, 64
+    q = torch.empty(B, H, T, d, dtype=torch.bfloat16, device=DEV)
+    k, v = (torch.empty(B, H, Tk, d, dtype=torch.bfloat16, device=DEV) for _ in range(2))
+    n = fa.splitkv_splits(B, H, T, Tk, d)
+    assert n > 1
+    ws = torch.empty(fa.splitkv_workspace_bytes(B, H, T, d, n), dtype=torch.uint8, device=DEV)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, T, dtype=torch.float32, device=DEV)
+
+    def refill(seed):
+        qb, _, _ = make_qkv(B, H, T, d, seed=seed)
+        _, kb, vb = make_qkv(B, H, Tk, d, seed=seed + 1)
+        for dst, src in zip((q, k, v), (qb, kb, vb)):
+            dst.copy_(to_torch_bf16(src, DEV))
+
+    refill(2)
+    g = capture(lambda: fa.fwd_splitkv(q, k, v, causal=True, n_splits=n, out=o, lse=lse, workspace=ws))
+    for r in range(REPLAYS):
+        refill(200 + 2 * r)
+        o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        o_e, lse_e = fa.fwd_splitkv(q, k, v, causal=True, n_splits=n)
+        torch.cuda.synchronize()
+        assert_same(o, o_e, f"o, replay {r}")
+        assert_same(lse, lse_e, f"lse, replay {r}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_bwd_graph_replays(d):
+    # the forward and both backward kernels in one graph
+    B, H, T = 1, 3, 700
+    q, k, v, do = (torch.empty(B, H, T, d, dtype=torch.bfloat16, device=DEV) for _ in range(4))
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    lse, delta = (torch.empty(B, H, T, dtype=torch.float32, device=DEV) for _ in range(2))
+
+    def step():
+        fa.fwd(q, k, v, causal=True, out=o, lse=lse)
+        fa.bwd(q, k, v, o, lse, do, causal=True, dq=dq, dk=dk, dv=dv, delta=delta)
+
+    fill((q, k, v), B, H, T, d, seed=3)
+    fill((do,), B, H, T, d, seed=4)
+    g = capture(step)
+    for r in range(REPLAYS):
+        fill((q, k, v), B, H, T, d, seed=300 + r)
+        fill((do,), B, H, T, d, seed=400 + r)
+        for t in (dq, dk, dv):
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        o_e, lse_e = fa.fwd(q, k, v, causal=True)
+        got = fa.bwd(q, k, v, o_e, lse_e, do, causal=True)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dv", "delta"), (dq, dk, dv, delta), got):
+            assert_same(a, b, f"{name}, replay {r}")
