@@ -52,7 +52,27 @@ int fold_grid(int64_t n, int threads, int splits, dim3* grid) {
 }
 
 using KernelFn = void (*)(const __bf16*, const __bf16*, const __bf16*, __bf16*, float*, int, int, int,
-                          float, const uint8_t*, int, int, int, int, int);
+                          float, const uint8_t*, int, int, int, int, int, int);
+
+// Heads per group within an XCD (see map_block). Causal: all of the XCD's heads interleaved, so
+// that the Q blocks with the most tiles of every head start first and the short ones fill the end
+// (grouping heads there left XCDs idle at the end of each group: 660-750 against 796 TFLOP/s at
+// B4 H12 T4096 d64). Non-causal, where every workgroup has the same work: the largest divisor of
+// B*H/8 whose K and V fit in half of an XCD's 4 MB L2, so that a group's Q blocks share its K/V
+// tiles in L2 (B4 H16 T8192 d128: 1105-1108 against 1076-1103 TFLOP/s on two boxes; non-causal
+// d64 shapes 0.2-0.4% faster). Used only when B*H is a multiple of 8.
+constexpr int64_t kHeadGroupBytes = int64_t{2} << 20;
+
+int head_group(int64_t BH, int64_t Tk, int d, bool causal) {
+  if (BH % 8 != 0) return 1;
+  const int per = (int)(BH / 8);
+  if (causal) return per;
+  const int64_t kv = std::max<int64_t>(Tk * d * 2 * 2, 1);
+  const int64_t gmax = std::max<int64_t>(1, kHeadGroupBytes / kv);
+  int g = per;
+  while (g > 1 && (g > gmax || per % g != 0)) --g;
+  return g;
+}
 
 struct TileEntry {
   int d, block_m, block_n, waves;
@@ -154,7 +174,7 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
   KernelFn fn = causal ? tile->causal_fn : tile->full_fn;
   return launch_kernel(fn, grid, dim3(64 * tile->waves), stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, T, nq, BH,
-                       scale_log2, (const uint8_t*)nullptr, 0, 0, 0, 0, 0);
+                       scale_log2, (const uint8_t*)nullptr, 0, 0, 0, 0, 0, head_group(BH, T, d, causal != 0));
 }
 
 // Block-sparse forward: the default tile shape (128 queries x 64 keys per tile, 4 waves) with the
@@ -198,7 +218,8 @@ int launch_sparse(const void* q, const void* k, const void* v, void* o, float* l
   else fn = causal ? &fa::fa_fwd_kernel<SparseFns<128>::Cc> : &fa::fa_fwd_kernel<SparseFns<128>::Cf>;
   return launch_kernel(fn, grid, dim3(256), stream, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, T, nq, BH,
-                       scale * fa::kLog2e, (const uint8_t*)block_mask, mask_heads, 0, 0, 0, 0);
+                       scale * fa::kLog2e, (const uint8_t*)block_mask, mask_heads, 0, 0, 0, 0,
+                       BH / 8);
 }
 
 // Partial forward over a key range: the default tile with the range selection and fp32 output.
@@ -257,7 +278,7 @@ int launch_ranges(const void* q, const void* k, const void* v, float* o_part, fl
   return launch_kernel(fn, grid, dim3(256), stream,
                        (const __bf16*)q, (const __bf16*)k, (const __bf16*)v, (__bf16*)o_part,
                        lse_part, T, nq, BH, scale * fa::kLog2e, (const uint8_t*)nullptr, 0, k_begin,
-                       k_end, Tk, k_chunk);
+                       k_end, Tk, k_chunk, BH / 8);
 }
 
 int launch_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part, int B,

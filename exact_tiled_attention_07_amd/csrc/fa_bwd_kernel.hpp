@@ -170,7 +170,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_bwd_dq_kernel(
   const int bid = block_index((int64_t)nq * BH);
   if (bid < 0) return;
   int qblk, bh;
-  map_block<C::CAUSAL>(bid, nq, BH, qblk, bh);
+  map_block<C::CAUSAL>(bid, nq, BH, BH >> 3, qblk, bh);
   const int q0 = qblk * BM;
   const int64_t head_off = (int64_t)bh * T * D;
   const char* kg = reinterpret_cast<const char*>(k + head_off);
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_bwd_dkdv_kernel(
   const int bid = block_index((int64_t)nk * BH);
   if (bid < 0) return;
   int kblk, bh;
-  map_block<false>(bid, nk, BH, kblk, bh);  // in rank order: the earliest key blocks (most Q tiles) first
+  map_block<false>(bid, nk, BH, BH >> 3, kblk, bh);  // in rank order: the earliest key blocks (most Q tiles) first
   const int k0 = kblk * BM;
   const int64_t head_off = (int64_t)bh * T * D;
   const char* qg = reinterpret_cast<const char*>(q + head_off);

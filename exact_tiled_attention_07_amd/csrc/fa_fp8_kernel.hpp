@@ -100,7 +100,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_fp8_kernel(
   const int bid = block_index((int64_t)nq * BH);
   if (bid < 0) return;
   int qblk, bh;
-  map_block<C::CAUSAL>(bid, nq, BH, qblk, bh);
+  map_block<C::CAUSAL>(bid, nq, BH, BH >> 3, qblk, bh);
   const int q0 = qblk * BM;
   const int64_t head_off = (int64_t)bh * T * D;  // elements (= bytes of the E4M3 tensors)
   const char* kg = reinterpret_cast<const char*>(k + head_off);

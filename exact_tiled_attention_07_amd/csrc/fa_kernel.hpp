@@ -210,9 +210,6 @@ __device__ __forceinline__ void vmem_wait() {  // all but the newest N vector-me
 }
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-// Map the flat workgroup id to (Q block, batch*head). Workgroups are handed to the 8 XCDs round
-// robin, so when B*H is a multiple of 8 each XCD gets its own set of heads (their K/V stay in that
-// XCD's L2), and within an XCD the Q blocks with the most K/V tiles start first.
 // Flat index of this workgroup among n. The dispatch counts work-items per grid dimension in 32
 // bits, so a launch of more workgroups than one dimension holds folds them into x (a multiple of
 // 8, which keeps the XCD round robin of the flat index) and z; workgroups past n get -1 and exit.
@@ -221,13 +218,20 @@ __device__ __forceinline__ int block_index(int64_t n) {
   return b < n ? (int)b : -1;
 }
 
+// Map the flat workgroup id to (Q block, batch*head). Workgroups are handed to the 8 XCDs round
+// robin, so when B*H is a multiple of 8 each XCD gets its own set of heads (their K/V stay in that
+// XCD's L2). Within an XCD the heads run in groups of hg (hg divides B*H/8): a group's Q blocks,
+// interleaved over its heads and the ones with the most K/V tiles first, are dispatched before the
+// next group's, so that only the K/V of hg heads compete for the XCD's L2 at a time. hg = B*H/8
+// interleaves all of the XCD's heads.
 template <bool CAUSAL>
-__device__ __forceinline__ void map_block(int bid, int nq, int BH, int& qblk, int& bh) {
+__device__ __forceinline__ void map_block(int bid, int nq, int BH, int hg, int& qblk, int& bh) {
   int rank;
   if ((BH & 7) == 0) {
-    const int xcd = bid & 7, slot = bid >> 3, per = BH >> 3;
-    rank = slot / per;
-    bh = (slot - rank * per) * 8 + xcd;
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int span = hg * nq, g = slot / span, s = slot - g * span;
+    rank = s / hg;
+    bh = (g * hg + (s - rank * hg)) * 8 + xcd;
   } else {
     rank = bid / BH;
     bh = bid - rank * BH;
@@ -240,7 +244,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int T, int nq, int BH, float scale_log2,
     const uint8_t* __restrict__ bmask, int mask_heads, int k_begin, int k_end, int t_keys,
-    int k_chunk) {
+    int k_chunk, int head_group) {
   constexpr int D = C::D, QB = C::QB, NW = C::NW, BN = C::BN, BM = C::BM;
   constexpr int KB = C::KB, CB = C::CB, PT = C::PT, KSTEPS = C::KSTEPS, RB = C::ROW_BYTES;
   constexpr int NS_QK = C::NS_QK, NS = C::NS, PD = C::PD;
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_kernel(
   const int bid = block_index((int64_t)nq * BH);
   if (bid < 0) return;
   int qblk, bh;
-  map_block<C::CAUSAL>(bid, nq, BH, qblk, bh);
+  map_block<C::CAUSAL>(bid, nq, BH, head_group, qblk, bh);
   const int q0 = qblk * BM;
   // T is the number of queries. A key range may come from a longer sequence of Tk keys (queries
   // then sit at its end: query i is at key position i + coff, the causal diagonal shifted by coff),
