@@ -108,14 +108,22 @@ const TileEntry* find_tile(int d, int block_m, int block_n, int waves) {
   return nullptr;
 }
 
-// Workgroups of the 128-query default below which short sequences take the key split: with fewer
-// than two such workgroups per compute unit the chip is under-filled and the last Q block of each
-// head (which visits every K/V tile of the head) sets the time; splitting its keys between two
-// waves halves that path and doubles the workgroups.
-constexpr int64_t kKeySplitBelow = 512;
+// When d = 64 launches take the key split (two waves per 32-query block, each on every other K/V
+// tile, 64 queries and 64 KB of LDS per workgroup) instead of the 128-query default. The split
+// halves the path of a head's last Q block, which visits every K/V tile of the head in turn, at the
+// cost of twice the workgroups (each with its prologue, epilogue and merge) and two workgroups per
+// compute unit instead of three. Fitted on measured causal shapes (split / default time, grid = the
+// default's workgroups, nq = its Q blocks per head): nq 8: 0.75-0.83 up to grid 288, 1.00 at 384,
+// 1.13 at 768; nq 16-128: 0.70-0.85 up to grid 384, 0.93-0.94 at 512, 1.03-1.05 at 768; nq 4: no gain.
+// Non-causal (every workgroup the same work): 0.82-0.95 up to grid 384.
+bool take_key_split(int T, int64_t BH, bool causal) {
+  const int64_t nq = (T + 127) / 128, grid = nq * BH;
+  if (causal) return nq >= 8 && grid < std::min<int64_t>(40 * nq, 640);
+  return grid < 512;
+}
 
-const TileEntry* default_tile(int d, int T, int64_t BH) {
-  if (d == 64 && (int64_t)((T + 127) / 128) * BH < kKeySplitBelow) {
+const TileEntry* default_tile(int d, int T, int64_t BH, bool causal) {
+  if (d == 64 && take_key_split(T, BH, causal)) {
     const TileEntry* ks = find_tile(64, 64, 64, 4);
     if (ks) return ks;
   }
@@ -132,9 +140,10 @@ int check_sizes(int B, int H, int T, int d) {
   return FA_OK;
 }
 
-int resolve_tile(int d, int T, int64_t BH, int block_m, int block_n, int waves, const TileEntry** out) {
+int resolve_tile(int d, int T, int64_t BH, bool causal, int block_m, int block_n, int waves,
+                 const TileEntry** out) {
   if (block_m == 0 && block_n == 0 && waves == 0) {
-    *out = default_tile(d, T, BH);
+    *out = default_tile(d, T, BH, causal);
   } else {
     if (block_m <= 0 || block_n <= 0 || waves <= 0) return FA_ERR_TILE;
     *out = find_tile(d, block_m, block_n, waves);
@@ -154,7 +163,7 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (rc != FA_OK) return rc;
   if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
   const TileEntry* tile = nullptr;
-  rc = resolve_tile(d, T, (int64_t)B * H, block_m, block_n, waves, &tile);
+  rc = resolve_tile(d, T, (int64_t)B * H, causal != 0, block_m, block_n, waves, &tile);
   if (rc != FA_OK) return rc;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGNMENT;
   if ((uintptr_t)lse & 3u) return FA_ERR_ALIGNMENT;
@@ -545,7 +554,7 @@ int fa_fwd_plan(int B, int H, int T, int d, int causal, int block_m, int block_n
   int rc = check_sizes(B, H, T, d);
   if (rc != FA_OK) return rc;
   const TileEntry* tile = nullptr;
-  rc = resolve_tile(d, T, (int64_t)B * H, block_m, block_n, waves, &tile);
+  rc = resolve_tile(d, T, (int64_t)B * H, causal != 0, block_m, block_n, waves, &tile);
   if (rc != FA_OK) return rc;
   fa_plan_info p;
   p.block_m = tile->block_m;

@@ -134,13 +134,19 @@ def test_plan_default_and_tile_counts():
 
 
 def test_plan_key_split_for_short_sequences():
-    # d = 64 problems whose 128-query grid is below 512 workgroups take the key split
-    c3 = fa.plan(4, 12, 1024, 64, True)  # 8 x 48 = 384 workgroups of 128 queries
-    assert (c3["key_split"], c3["block_m"], c3["waves"], c3["lds_bytes"]) == (2, 64, 4, 65536)
-    assert c3["grid"] == 16 * 48
-    assert fa.plan(2, 12, 1000, 64, True)["key_split"] == 2
-    assert fa.plan(4, 12, 2048, 64, True)["key_split"] == 1   # 16 x 48 = 768
-    assert fa.plan(4, 12, 4096, 64, True)["key_split"] == 1
+    # d = 64 takes the key split for short grids (nq = ceil(T/128) Q blocks per head, grid = nq*B*H):
+    # causal when nq >= 8 and grid < min(40*nq, 640), non-causal when grid < 512
+    ks = fa.plan(3, 12, 1024, 64, True)  # nq 8, 288 workgroups of 128 queries
+    assert (ks["key_split"], ks["block_m"], ks["waves"], ks["lds_bytes"]) == (2, 64, 4, 65536)
+    assert ks["grid"] == 16 * 36
+    assert fa.plan(2, 12, 1000, 64, True)["key_split"] == 2   # nq 8, grid 192
+    assert fa.plan(4, 12, 1024, 64, True)["key_split"] == 1   # nq 8, grid 384 >= 320
+    assert fa.plan(1, 16, 4096, 64, True)["key_split"] == 2   # nq 32, grid 512 < 640
+    assert fa.plan(1, 24, 4096, 64, True)["key_split"] == 1   # grid 768
+    assert fa.plan(4, 12, 2048, 64, True)["key_split"] == 1   # grid 768
+    assert fa.plan(1, 12, 512, 64, True)["key_split"] == 1    # nq 4
+    assert fa.plan(4, 12, 1024, 64, False)["key_split"] == 2  # non-causal, grid 384
+    assert fa.plan(4, 12, 2048, 64, False)["key_split"] == 1  # non-causal, grid 768
     assert fa.plan(1, 1, 8, 128, True)["key_split"] == 1      # d = 128 never splits
     assert fa.plan(4, 12, 4096, 64, True, 64, 64, 4)["key_split"] == 2  # forced
     assert fa.plan(1, 1, 8, 64, True, 128, 64, 4)["key_split"] == 1

@@ -93,9 +93,10 @@ def test_configs_sampled(name):
 
 
 def test_many_heads_short_sequences():
-    # 2048 heads of T = 100 (a grid of 2048 x 1 workgroups of 128 queries), and of T = 30 with the
-    # key split (ceil(30/128) x 64 heads < 512), every row checked
-    for B, H, T in ((32, 64, 100), (4, 16, 30)):
+    # 2048 heads of T = 100 and 64 heads of T = 30 (one Q block per head: the 128-query launch), and
+    # 36 heads of T = 1000 (8 Q blocks per head, grid 288: the key split), every row checked
+    for B, H, T, split in ((32, 64, 100, 1), (4, 16, 30, 1), (1, 36, 1000, 2)):
+        assert fa.plan(B, H, T, 64, True)["key_split"] == split
         qb, kb, vb = make_qkv(B, H, T, 64, seed=B + H + T)
         full_check(qb, kb, vb, True, 0.125, f"B{B} H{H} T{T}")
 
@@ -161,7 +162,8 @@ def test_key_split_long_sequence(causal):
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("T", [1, 2, 31, 63, 64, 65, 127, 129, 255, 257, 1000])
 def test_ragged_and_tiny_lengths(T, causal, d):
-    # small problems: at d = 64 the default launch is the key split (two waves per query block)
+    # small problems, three heads: at d = 64 the non-causal ones and causal T = 1000 take the key
+    # split (two waves per query block), the other causal ones the 128-query launch
     qb, kb, vb = make_qkv(1, 3, T, d, seed=1000 + T + d)
     full_check(qb, kb, vb, causal, 1.0 / math.sqrt(d), f"T={T} d={d}")
 
