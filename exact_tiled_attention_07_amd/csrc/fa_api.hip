@@ -505,11 +505,13 @@ int fa_splitkv_splits(int B, int H, int T, int Tk, int d) {
   if (B <= 0 || H <= 0 || T <= 0 || Tk <= 0 || check_sizes(B, H, T, d) != FA_OK || Tk > FA_MAX_T)
     return 1;
   // as many workgroups as two per compute unit hold at once (not more: a second round would wait
-  // for the first), with at least 8 key tiles (512 keys) per range
+  // for the first), with at least 8 key tiles (512 keys) per range and at most 256 ranges: the
+  // merge reads a row's parts a few at a time, so for few rows many parts cost more latency than
+  // the finer split saves (one head, 2^20 keys: 90 us with 256 ranges, 99 us with 512)
   const int64_t base = (int64_t)((T + 127) / 128) * B * H;
   const int64_t want = 512 / base;
   const int64_t most = std::max(1, ((Tk + FA_PARTIAL_KEY_ALIGN - 1) / FA_PARTIAL_KEY_ALIGN) / 8);
-  return (int)std::max<int64_t>(1, std::min<int64_t>({want, most, FA_MERGE_MAX_PARTS}));
+  return (int)std::max<int64_t>(1, std::min<int64_t>({want, most, int64_t{256}}));
 }
 
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

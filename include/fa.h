@@ -200,7 +200,7 @@ int fa_merge(const float* o_parts, const float* lse_parts, int n_parts, void* o,
  * n_splits outside 1 .. FA_MERGE_MAX_PARTS) or the product does not fit in size_t. Host-only. */
 size_t fa_splitkv_workspace_bytes(int B, int H, int T, int d, int n_splits);
 /* A split count for these sizes that fills the GPU: enough key ranges for about 512 workgroups, each
- * range at least 8 tiles of 64 keys, at most FA_MERGE_MAX_PARTS. 1 for empty or out-of-range sizes.
+ * range at least 8 tiles of 64 keys, at most 256 ranges. 1 for empty or out-of-range sizes.
  * Host-only. */
 int fa_splitkv_splits(int B, int H, int T, int Tk, int d);
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,

@@ -293,6 +293,7 @@ def test_splitkv_split_count():
     lib = fa.lib()
     # few query blocks against many keys: split up to 512 workgroups, 512 keys per range at least
     assert lib.fa_splitkv_splits(1, 1, 1, 65536, 64) == 128
+    assert lib.fa_splitkv_splits(1, 1, 1, 1 << 20, 64) == 256   # at most 256 ranges
     assert lib.fa_splitkv_splits(4, 12, 1, 65536, 64) == 10
     assert lib.fa_splitkv_splits(4, 12, 4096, 4096, 64) == 1
     assert lib.fa_splitkv_splits(1, 1, 1, 100, 64) == 1

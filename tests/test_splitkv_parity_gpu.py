@@ -194,7 +194,7 @@ def test_splitkv_against_oracle(B, H, T, Tk, d, n, causal):
 @pytest.mark.parametrize("T,Tk,d", [(16, 1 << 22, 64), (1, (1 << 22) - 1, 128)])
 def test_splitkv_longest_keys(T, Tk, d):
     # the largest accepted key length (FA_MAX_T = 2^22; one short of it at d = 128, a ragged last
-    # tile) with the split count the library picks: 512 ranges of 8192 keys, merged in log space
+    # tile) with the split count the library picks: 256 ranges of 16384 keys, merged in log space
     B, H = 1, 1
     qb, kb, vb = cross_inputs(B, H, T, Tk, d, seed=8000 + d)
     scale = 1.0 / math.sqrt(d)
