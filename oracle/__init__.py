@@ -25,10 +25,11 @@ is zero are not visible, the way the causal mask hides the blocks above the diag
 "内核案例研究：Flash Attention", section "块稀疏注意力 V2 和 V3"); a row with no visible key gets
 ``O = 0`` and ``LSE = -inf``.
 
-Two functions are numpy float64 rather than C: ``merge_partials``, the log-space combine of partial
-results over disjoint key ranges (ijyty.com FlashAttention article, section 2.1), and
+Three functions are numpy float64 rather than C: ``merge_partials``, the log-space combine of
+partial results over disjoint key ranges (ijyty.com FlashAttention article, section 2.1),
 ``attention_fwd_cross``, the plain two-pass attention of T queries over a key range of a Tk-key
-sequence (one library matmul per head for the scores and one for P V).
+sequence (one library matmul per head for the scores and one for P V), and ``attention_bwd_rows``,
+the backward's definitions evaluated for selected query and key rows of long heads.
 
 ``attention_fwd_fp8`` decodes FP8 E4M3 codes exactly, applies the per-tensor descale factors in
 float64 and calls the float64 forward.
@@ -236,6 +237,65 @@ def attention_bwd_f64(q, k, v, do, causal: bool, scale: float, num_threads: int 
                                 B, H, T, d, int(bool(causal)), float(scale), int(num_threads))
     if rc != 0:
         raise RuntimeError(f"fa_ref_bwd_f64 failed with code {rc}")
+    return dq, dk, dv, delta
+
+
+def attention_bwd_rows(q_bits, k_bits, v_bits, do_bits, causal: bool, scale: float, q_rows, k_rows,
+                       block_rows: int = 512):
+    """The backward for selected rows, in numpy float64, for heads too long for ``attention_bwd``.
+
+    ``q_rows`` and ``k_rows`` are flat row indices ``(b*H + h)*T + i``. Returns ``(dq, dk, dv,
+    delta)``: ``dq`` float64 ``[len(q_rows), d]`` (gradient of query row i), ``dk`` and ``dv``
+    ``[len(k_rows), d]`` (gradients of key/value row j), and ``delta`` ``[len(q_rows)]``
+    (``D_i = dO_i . O_i``). The same definitions as ``attention_bwd`` (learn-llm.fim.ai
+    "手写 FlashAttention：拆开 SDPA 这个黑盒", STEP 4; ijyty.com FlashAttention article, section
+    2.2), evaluated row by row: for each head that a requested row belongs to, every query row's
+    LSE_i and D_i come from its own two-pass softmax (rows taken a block at a time only to bound
+    memory), then
+        P_ij = exp(scale q_i.k_j - LSE_i),  dP_ij = dO_i.v_j,  dS_ij = P_ij (dP_ij - D_i),
+        dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i
+    over the visible pairs (j <= i when causal).
+    """
+    q, k = _bf16_to_f64(_as_bf16_bits(q_bits, "q")), _bf16_to_f64(_as_bf16_bits(k_bits, "k"))
+    v, do = _bf16_to_f64(_as_bf16_bits(v_bits, "v")), _bf16_to_f64(_as_bf16_bits(do_bits, "do"))
+    if not (q.shape == k.shape == v.shape == do.shape):
+        raise ValueError(f"q/k/v/do shapes differ: {q.shape} {k.shape} {v.shape} {do.shape}")
+    B, H, T, d = q.shape
+    qr = np.asarray(q_rows, dtype=np.int64).reshape(-1)
+    kr = np.asarray(k_rows, dtype=np.int64).reshape(-1)
+    dq = np.empty((qr.size, d)); dk = np.empty((kr.size, d)); dv = np.empty((kr.size, d))
+    delta = np.empty(qr.size)
+    idx = np.arange(T)
+    for head in sorted(set((qr // T).tolist()) | set((kr // T).tolist())):
+        b, h = divmod(head, H)
+        Q, K, V, dO = q[b, h], k[b, h], v[b, h], do[b, h]
+        lse, D = np.empty(T), np.empty(T)
+        for i0 in range(0, T, block_rows):
+            i1 = min(i0 + block_rows, T)
+            kend = i1 if causal else T  # keys past the block's last row are hidden from all of it
+            s = scale * (Q[i0:i1] @ K[:kend].T)
+            if causal:
+                s = np.where(idx[None, :kend] > idx[i0:i1, None], -np.inf, s)
+            m = s.max(axis=1)
+            e = np.exp(s - m[:, None])
+            l = e.sum(axis=1)
+            o = (e @ V[:kend]) / l[:, None]
+            lse[i0:i1] = m + np.log(l)
+            D[i0:i1] = (dO[i0:i1] * o).sum(axis=1)
+        for n in np.nonzero(qr // T == head)[0]:
+            i = int(qr[n] % T)
+            vis = idx <= i if causal else np.ones(T, dtype=bool)
+            p = np.exp(scale * (K[vis] @ Q[i]) - lse[i])
+            ds = p * (V[vis] @ dO[i] - D[i])
+            dq[n] = scale * (ds @ K[vis])
+            delta[n] = D[i]
+        for n in np.nonzero(kr // T == head)[0]:
+            j = int(kr[n] % T)
+            vis = idx >= j if causal else np.ones(T, dtype=bool)
+            p = np.exp(scale * (Q[vis] @ K[j]) - lse[vis])
+            dv[n] = p @ dO[vis]
+            ds = p * (dO[vis] @ V[j] - D[vis])
+            dk[n] = scale * (ds @ Q[vis])
     return dq, dk, dv, delta
 
 

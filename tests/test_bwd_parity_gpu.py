@@ -112,6 +112,35 @@ def test_bwd_long_sequence():
     check(*inputs(1, 4, 4096, 4, sigma=2.0), True, 0.125, "T=4096 sigma2 (4 heads)")
 
 
+@pytest.mark.parametrize("B,H,T,d,causal", [(1, 2, 16384, 64, True), (1, 1, 8192, 128, False)])
+def test_bwd_long_heads_sampled_rows(B, H, T, d, causal):
+    # long heads (the dK/dV kernel's first key block walks 256 Q tiles at T = 16384) against the
+    # row entry of the oracle on sampled query and key rows: first and last rows, tile edges, the
+    # middle and random rows of every head
+    qb, kb, vb, dob = inputs(B, H, T, 90 + d, sigma=1.5, d=d)
+    scale = 1.0 / math.sqrt(d)
+    say(f"[gpu bwd] long heads B={B} H={H} T={T} d={d} causal={causal}")
+    q, k, v, do = (to_torch_bf16(x, DEV) for x in (qb, kb, vb, dob))
+    o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
+    dq, dk, dv, delta = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(T + d)
+    rows = sorted({bh * T + i for bh in range(B * H)
+                   for i in [0, 1, 63, 64, 127, 128, T // 2, T - 2, T - 1] + rng.integers(0, T, 12).tolist()})
+    idx = torch.as_tensor(rows, dtype=torch.int64, device=DEV)
+    got = [t.reshape(-1, d).index_select(0, idx).float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
+    got.append(delta.reshape(-1).index_select(0, idx).cpu().numpy().astype(np.float64))
+    ref = oracle.attention_bwd_rows(qb, kb, vb, dob, causal, scale, rows, rows)
+    qa, ka, va, da = (np.abs(bf16_bits_to_f32(x).astype(np.float64)) for x in (qb, kb, vb, dob))
+    cancel = d * 2.0 ** -24 * float(da.sum(axis=-1).max()) * float(va.max())
+    floors = (2 * scale * float(ka.max()) * cancel, 2 * scale * float(qa.max()) * cancel, 0.0, 0.0)
+    n = len(rows)
+    for name, g, r, a in zip(("dq", "dk", "dv", "delta"), got, ref, floors):
+        shape = (1, 1, n, d) if name != "delta" else (1, 1, n)
+        st = grad_tolerance(name, g.reshape(shape), r.reshape(shape), a)
+        say(f"[gpu bwd] long heads {name}: {st['max_ratio']:.4f}/{st['rms_ratio']:.4f}")
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_bwd_other_scales_and_wide_scores(causal):
     check(*inputs(2, 2, 300, 77), causal, 0.01, "scale=0.01")

@@ -9,6 +9,8 @@ B3 exact identities of the softmax Jacobian: sum_j dV_j = sum_i dO_i (rows of P 
 B4 special cases: a single visible key, constant V rows, Q = 0, dO = 0.
 B5 the float64 forward used by B1 equals the bf16 forward oracle bit for bit on bf16 inputs, and
    the bf16 backward entry point equals the float64 one on the widened inputs.
+B6 the row entry for long heads (numpy) equals the whole-head backward (C, pinned by B1-B5) on
+   every query and key row.
 A plausible slip in the backward (a dropped delta term, a missing scale, a transposed operand, a
 wrong mask bound) fails B1 and B2; B3 catches a dropped normalisation.
 """
@@ -139,3 +141,20 @@ def test_bwd_entry_points_reject_bad_input():
     empty = np.zeros((1, 1, 0, 8), dtype=np.uint16)
     out = oracle.attention_bwd(empty, empty, empty, empty, True, 0.5)
     assert all(x.size == 0 for x in out)
+
+
+@pytest.mark.parametrize("B,H,T,d,causal", [(1, 2, 300, 64, True), (1, 2, 300, 64, False), (2, 1, 130, 128, True),
+                                            (1, 1, 1, 64, True), (1, 1, 65, 16, False)])
+def test_b6_row_entry_matches_the_whole_head_oracle(B, H, T, d, causal):
+    # attention_bwd_rows (numpy, rows) against attention_bwd (C, whole heads, pinned by B1-B5) on
+    # every query and key row; the row blocking is made smaller than T to cross block edges
+    qb, kb, vb = make_qkv(B, H, T, d, seed=60 + T + d, sigma=1.5)
+    dob = make_qkv(B, H, T, d, seed=61 + T)[0]
+    scale = d ** -0.5
+    dq, dk, dv, delta = oracle.attention_bwd(qb, kb, vb, dob, causal, scale)
+    rows = np.arange(B * H * T)
+    rq, rk, rv, rd = oracle.attention_bwd_rows(qb, kb, vb, dob, causal, scale, rows, rows[::-1], block_rows=64)
+    np.testing.assert_allclose(rq, dq.reshape(-1, d), rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(rk, dk.reshape(-1, d)[::-1], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(rv, dv.reshape(-1, d)[::-1], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(rd, delta.reshape(-1), rtol=1e-10, atol=1e-12)
