@@ -60,7 +60,8 @@ using KernelFn = void (*)(const __bf16*, const __bf16*, const __bf16*, __bf16*, 
 // B4 H12 T4096 d64). Non-causal, where every workgroup has the same work: the largest divisor of
 // B*H/8 whose K and V fit in half of an XCD's 4 MB L2, so that a group's Q blocks share its K/V
 // tiles in L2 (B4 H16 T8192 d128: 1105-1108 against 1076-1103 TFLOP/s on two boxes; non-causal
-// d64 shapes 0.2-0.4% faster). Used only when B*H is a multiple of 8.
+// d64 shapes 0.2-0.4% faster). The backward kernels take the same groups (its B4 H16 T8192 d128:
+// 680-682 against 663-665 TFLOP/s on one box). Used only when B*H is a multiple of 8.
 constexpr int64_t kHeadGroupBytes = int64_t{2} << 20;
 
 int head_group(int64_t BH, int64_t Tk, int d, bool causal) {
@@ -465,15 +466,19 @@ int launch_bwd_kernels(const void* q, const void* k, const void* v, const void* 
   dim3 grid;
   if (fold_grid((int64_t)nb * BH, Cc::THREADS, 1, &grid) != FA_OK) return FA_ERR_INVALID_ARG;
   const float scale_log2 = scale * fa::kLog2e;
+  // heads per group within an XCD, as for the forward: the dQ kernel streams a head's K and V, the
+  // dK/dV kernel its Q and dO (as many bytes)
+  const int hg = head_group(BH, T, D, causal != 0);
   auto dq_fn = causal ? &fa::fa_bwd_dq_kernel<Cc> : &fa::fa_bwd_dq_kernel<Cf>;
   auto dkdv_fn = causal ? &fa::fa_bwd_dkdv_kernel<Cc> : &fa::fa_bwd_dkdv_kernel<Cf>;
   const int rc = launch_kernel(dq_fn, grid, dim3(Cc::THREADS), stream, (const __bf16*)q,
                                (const __bf16*)k, (const __bf16*)v, (const __bf16*)o, lse,
-                               (const __bf16*)dout, (__bf16*)dq, delta, T, nb, BH, scale, scale_log2);
+                               (const __bf16*)dout, (__bf16*)dq, delta, T, nb, BH, scale, scale_log2,
+                               hg);
   if (rc != FA_OK) return rc;
   return launch_kernel(dkdv_fn, grid, dim3(Cc::THREADS), stream, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dout,
-                       (const float*)delta, (__bf16*)dk, (__bf16*)dv, T, nb, BH, scale, scale_log2);
+                       (const float*)delta, (__bf16*)dk, (__bf16*)dv, T, nb, BH, scale, scale_log2, hg);
 }
 
 }  // namespace

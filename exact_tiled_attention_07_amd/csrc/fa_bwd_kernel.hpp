@@ -158,7 +158,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_bwd_dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ o, const float* __restrict__ lse, const __bf16* __restrict__ dout,
     __bf16* __restrict__ dq, float* __restrict__ delta, int T, int nq, int BH, float scale,
-    float scale_log2) {
+    float scale_log2, int head_group) {
   constexpr int D = C::D, BN = C::BN, BM = C::BM, KB = C::KB, CB = C::CB, PT = C::PT;
   constexpr int KSTEPS = C::KSTEPS, RB = C::ROW_BYTES, TB = C::TILE_BYTES;
   __shared__ __attribute__((aligned(1024))) char smem[4 * TB];  // K ring (2 tiles), V ring (2 tiles)
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_bwd_dq_kernel(
   const int bid = block_index((int64_t)nq * BH);
   if (bid < 0) return;
   int qblk, bh;
-  map_block<C::CAUSAL>(bid, nq, BH, BH >> 3, qblk, bh);
+  map_block<C::CAUSAL>(bid, nq, BH, head_group, qblk, bh);
   const int q0 = qblk * BM;
   const int64_t head_off = (int64_t)bh * T * D;
   const char* kg = reinterpret_cast<const char*>(k + head_off);
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* __restrict__ lse, const __bf16* __restrict__ dout, const float* __restrict__ delta,
     __bf16* __restrict__ dk, __bf16* __restrict__ dv, int T, int nk, int BH, float scale,
-    float scale_log2) {
+    float scale_log2, int head_group) {
   constexpr int D = C::D, BN = C::BN, BM = C::BM, KB = C::KB, CB = C::CB;
   constexpr int KSTEPS = C::KSTEPS, RB = C::ROW_BYTES, TB = C::TILE_BYTES, SB = C::STATS_BYTES;
   // Q ring (2 tiles), dO ring (2 tiles), statistics ring (2 x [LSE | D] of a Q tile)
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_bwd_dkdv_kernel(
   const int bid = block_index((int64_t)nk * BH);
   if (bid < 0) return;
   int kblk, bh;
-  map_block<false>(bid, nk, BH, BH >> 3, kblk, bh);  // in rank order: the earliest key blocks (most Q tiles) first
+  map_block<false>(bid, nk, BH, head_group, kblk, bh);  // in rank order: the earliest key blocks (most Q tiles) first
   const int k0 = kblk * BM;
   const int64_t head_off = (int64_t)bh * T * D;
   const char* qg = reinterpret_cast<const char*>(q + head_off);
