@@ -61,14 +61,16 @@ using KernelFn = void (*)(const __bf16*, const __bf16*, const __bf16*, __bf16*, 
 // B*H/8 whose K and V fit in half of an XCD's 4 MB L2, so that a group's Q blocks share its K/V
 // tiles in L2 (B4 H16 T8192 d128: 1105-1108 against 1076-1103 TFLOP/s on two boxes; non-causal
 // d64 shapes 0.2-0.4% faster). The backward kernels take the same groups (its B4 H16 T8192 d128:
-// 680-682 against 663-665 TFLOP/s on one box). Used only when B*H is a multiple of 8.
+// 680-682 against 663-665 TFLOP/s on one box), and so does the FP8 forward with its one-byte K and V
+// (elem_bytes = 1; B4 H16 T8192 d128: 1801-1811 against 1784-1785). Used only when B*H is a
+// multiple of 8.
 constexpr int64_t kHeadGroupBytes = int64_t{2} << 20;
 
-int head_group(int64_t BH, int64_t Tk, int d, bool causal) {
+int head_group(int64_t BH, int64_t Tk, int d, bool causal, int elem_bytes = 2) {
   if (BH % 8 != 0) return 1;
   const int per = (int)(BH / 8);
   if (causal) return per;
-  const int64_t kv = std::max<int64_t>(Tk * d * 2 * 2, 1);
+  const int64_t kv = std::max<int64_t>(Tk * d * elem_bytes * 2, 1);
   const int64_t gmax = std::max<int64_t>(1, kHeadGroupBytes / kv);
   int g = per;
   while (g > 1 && (g > gmax || per % g != 0)) --g;
@@ -406,7 +408,7 @@ int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   dim3 grid;
   if (fold_grid((int64_t)nq * BH, 256, 1, &grid) != FA_OK) return FA_ERR_INVALID_ARG;
   using Fn8 = void (*)(const uint8_t*, const uint8_t*, const uint8_t*, __bf16*, float*, int, int, int,
-                       float, float);
+                       float, float, int);
   Fn8 fn;
   if (d == 64)
     fn = causal ? &fa::fa_fwd_fp8_kernel<fa::Fp8Cfg<64, true>> : &fa::fa_fwd_fp8_kernel<fa::Fp8Cfg<64, false>>;
@@ -415,7 +417,7 @@ int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
   static_assert(fa::Fp8Cfg<64, true>::BM == 128 && fa::Fp8Cfg<128, true>::BM == 128, "Q block");
   return launch_kernel(fn, grid, dim3(256), stream, (const uint8_t*)q,
                        (const uint8_t*)k, (const uint8_t*)v, (__bf16*)o, lse, T, nq, BH, (float)sl2,
-                       v_descale);
+                       v_descale, head_group(BH, T, d, causal != 0, 1));
 }
 
 template <int D>

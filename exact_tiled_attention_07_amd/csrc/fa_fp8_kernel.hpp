@@ -85,7 +85,7 @@ template <class C>
 __global__ __launch_bounds__(C::THREADS) void fa_fwd_fp8_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ k, const uint8_t* __restrict__ v,
     __bf16* __restrict__ o, float* __restrict__ lse, int T, int nq, int BH, float scale_log2,
-    float v_descale) {
+    float v_descale, int head_group) {
   constexpr int D = C::D, NW = C::NW, BN = C::BN, BM = C::BM, RB = C::ROW_BYTES;
   constexpr int KB = C::KB, CB = C::CB, KS = C::KSTEPS;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(C::THREADS) void fa_fwd_fp8_kernel(
   const int bid = block_index((int64_t)nq * BH);
   if (bid < 0) return;
   int qblk, bh;
-  map_block<C::CAUSAL>(bid, nq, BH, BH >> 3, qblk, bh);
+  map_block<C::CAUSAL>(bid, nq, BH, head_group, qblk, bh);
   const int q0 = qblk * BM;
   const int64_t head_off = (int64_t)bh * T * D;  // elements (= bytes of the E4M3 tensors)
   const char* kg = reinterpret_cast<const char*>(k + head_off);
