@@ -111,24 +111,34 @@ const TileEntry* find_tile(int d, int block_m, int block_n, int waves) {
   return nullptr;
 }
 
-// When d = 64 launches take the key split (two waves per 32-query block, each on every other K/V
-// tile, 64 queries and 64 KB of LDS per workgroup) instead of the 128-query default. The split
-// halves the path of a head's last Q block, which visits every K/V tile of the head in turn, at the
-// cost of twice the workgroups (each with its prologue, epilogue and merge) and two workgroups per
-// compute unit instead of three. Fitted on measured causal shapes (split / default time, grid = the
-// default's workgroups, nq = its Q blocks per head): nq 8: 0.75-0.83 up to grid 288, 1.00 at 384,
-// 1.13 at 768; nq 16-128: 0.70-0.85 up to grid 384, 0.93-0.94 at 512, 1.03-1.05 at 768; nq 4: no gain.
-// Non-causal (every workgroup the same work): 0.82-0.95 up to grid 384.
-bool take_key_split(int T, int64_t BH, bool causal) {
-  const int64_t nq = (T + 127) / 128, grid = nq * BH;
-  if (causal) return nq >= 8 && grid < std::min<int64_t>(40 * nq, 640);
-  return grid < 512;
+// The d = 64 default depends on the grid of the 128 x 64 launch (nq = ceil(T/128) Q blocks per head,
+// grid = nq * B * H workgroups). Measured on one box (time relative to 128 x 64 x 4):
+// - the key split (two waves per 32-query block, each on every other K/V tile; 64 queries and 64 KB
+//   of LDS per workgroup, two per compute unit) halves the path of a head's last Q block at the cost
+//   of twice the workgroups. Causal: 0.73-0.75 at nq 8 up to grid 288, 0.77-0.83 at nq 16-32 and
+//   grid 384, but 0.96 at nq 8 and grid 384 and 0.93-0.94 at grid 512. Non-causal: 0.77 at grid 96,
+//   0.91-0.95 at grid 384.
+// - 128-key tiles (234 VGPRs, two workgroups per compute unit, half the barriers and loop steps per
+//   key) win on short heads: causal 0.89-0.92 at grid 96-512, 0.96-0.98 at nq 8 up to grid 1536 and
+//   at nq 16 and grid 768; non-causal 0.89-0.93 at grid 384; but 1.01-1.07 at nq 4, at nq 16 and grid
+//   1536 and at nq 32 and grid 1536.
+// The rules below take the faster of the three in each measured region.
+bool take_key_split(int64_t nq, int64_t grid, bool causal) {
+  if (causal) return nq >= 8 && grid <= 384 && (nq >= 16 || grid <= 288);
+  return grid <= 256;
+}
+
+bool take_wide_key_tiles(int64_t nq, int64_t grid) {
+  return nq >= 5 && (nq <= 8 || grid <= 768);
 }
 
 const TileEntry* default_tile(int d, int T, int64_t BH, bool causal) {
-  if (d == 64 && take_key_split(T, BH, causal)) {
-    const TileEntry* ks = find_tile(64, 64, 64, 4);
-    if (ks) return ks;
+  if (d == 64) {
+    const int64_t nq = (T + 127) / 128, grid = nq * BH;
+    const TileEntry* t = nullptr;
+    if (take_key_split(nq, grid, causal)) t = find_tile(64, 64, 64, 4);
+    else if (take_wide_key_tiles(nq, grid)) t = find_tile(64, 128, 128, 4);
+    if (t) return t;
   }
   for (const TileEntry& t : kTiles)
     if (t.d == d) return &t;

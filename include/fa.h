@@ -69,11 +69,13 @@ typedef enum fa_status {
  *   causal   nonzero: query i sees keys 0..i (the causal mask); zero: it sees all T keys
  *   scale    finite and > 0; the scores are scale * q.k (1/sqrt(d) for standard attention)
  *   stream   hipStream_t to launch on (NULL: default stream)
- * The launch depends on the sizes (fa_fwd_plan reports it): 128 queries per workgroup, or, at d = 64
- * for short grids, the key split: two waves per 32-query block each take every other K/V tile and
- * merge their partial results in log space (ijyty.com FlashAttention article, section 2.1). With
- * nq = ceil(T/128) query blocks per head and grid = nq*B*H, the key split is taken when causal and
- * nq >= 8 and grid < min(40*nq, 640), or when non-causal and grid < 512. Both give the exact result up to rounding order; a fixed problem always takes the same
+ * The launch depends on the sizes (fa_fwd_plan reports it): 128 queries x 64 keys per workgroup and
+ * tile, or, at d = 64 for short sequences, one of two others. With nq = ceil(T/128) query blocks
+ * per head and grid = nq*B*H:
+ *   - the key split (two waves per 32-query block each take every other K/V tile and merge their
+ *     partial results in log space; ijyty.com FlashAttention article, section 2.1) when causal,
+ *     nq >= 8, grid <= 384 and (nq >= 16 or grid <= 288), or non-causal and grid <= 256;
+ *   - else 128-key tiles when nq >= 5 and (nq <= 8 or grid <= 768). Both give the exact result up to rounding order; a fixed problem always takes the same
  * launch, so repeated calls are bit-identical.
  * Returns FA_OK or a negative fa_status.
  */
@@ -104,8 +106,8 @@ typedef struct fa_plan_info {
   int lds_bytes;   /* LDS per workgroup: double-buffered K and V tiles */
   long long kv_tiles; /* K/V tiles processed by all workgroups (fully masked ones skipped) */
   int key_split;   /* 1, or 2: two waves share each 32-query block, each taking every other K/V tile,
-                      and merge their partial results in log space (the default at d = 64 for
-                      the short grids described at fa_fwd) */
+                      and merge their partial results in log space (a default at d = 64 for
+                      the short sequences described at fa_fwd) */
 } fa_plan_info;
 
 /*

@@ -133,21 +133,28 @@ def test_plan_default_and_tile_counts():
     assert fa.plan(0, 12, 1000, 64, True)["grid"] == 0
 
 
-def test_plan_key_split_for_short_sequences():
-    # d = 64 takes the key split for short grids (nq = ceil(T/128) Q blocks per head, grid = nq*B*H):
-    # causal when nq >= 8 and grid < min(40*nq, 640), non-causal when grid < 512
-    ks = fa.plan(3, 12, 1024, 64, True)  # nq 8, 288 workgroups of 128 queries
+def test_plan_default_tile_for_short_sequences():
+    # d = 64 picks among the key split, 128-key tiles and the 128 x 64 default by the grid of the
+    # 128 x 64 launch (nq = ceil(T/128) Q blocks per head, grid = nq*B*H)
+    def pick(B, H, T, causal):
+        p = fa.plan(B, H, T, 64, causal)
+        return "split" if p["key_split"] == 2 else f"{p['block_m']}x{p['block_n']}"
+    ks = fa.plan(3, 12, 1024, 64, True)  # nq 8, grid 288: the key split
     assert (ks["key_split"], ks["block_m"], ks["waves"], ks["lds_bytes"]) == (2, 64, 4, 65536)
     assert ks["grid"] == 16 * 36
-    assert fa.plan(2, 12, 1000, 64, True)["key_split"] == 2   # nq 8, grid 192
-    assert fa.plan(4, 12, 1024, 64, True)["key_split"] == 1   # nq 8, grid 384 >= 320
-    assert fa.plan(1, 16, 4096, 64, True)["key_split"] == 2   # nq 32, grid 512 < 640
-    assert fa.plan(1, 24, 4096, 64, True)["key_split"] == 1   # grid 768
-    assert fa.plan(4, 12, 2048, 64, True)["key_split"] == 1   # grid 768
-    assert fa.plan(1, 12, 512, 64, True)["key_split"] == 1    # nq 4
-    assert fa.plan(4, 12, 1024, 64, False)["key_split"] == 2  # non-causal, grid 384
-    assert fa.plan(4, 12, 2048, 64, False)["key_split"] == 1  # non-causal, grid 768
-    assert fa.plan(1, 1, 8, 128, True)["key_split"] == 1      # d = 128 never splits
+    assert pick(2, 12, 1000, True) == "split"     # nq 8, grid 192
+    assert pick(1, 12, 4096, True) == "split"     # nq 32, grid 384
+    assert pick(4, 12, 1024, True) == "128x128"   # nq 8, grid 384
+    assert pick(16, 12, 1024, True) == "128x128"  # nq 8, grid 1536
+    assert pick(4, 12, 2048, True) == "128x128"   # nq 16, grid 768
+    assert pick(8, 12, 2048, True) == "128x64"    # nq 16, grid 1536
+    assert pick(4, 12, 4096, True) == "128x64"    # nq 32, grid 1536
+    assert pick(4, 12, 512, True) == "128x64"     # nq 4
+    assert pick(1, 12, 1024, False) == "split"    # non-causal, grid 96
+    assert pick(4, 12, 1024, False) == "128x128"  # non-causal, grid 384
+    assert pick(4, 16, 8192, False) == "128x64"   # non-causal, grid 4096
+    assert fa.plan(1, 1, 8, 128, True)["key_split"] == 1      # d = 128: always 128 x 64
+    assert fa.plan(1, 1, 8, 128, True)["block_n"] == 64
     assert fa.plan(4, 12, 4096, 64, True, 64, 64, 4)["key_split"] == 2  # forced
     assert fa.plan(1, 1, 8, 64, True, 128, 64, 4)["key_split"] == 1
 
