@@ -235,6 +235,24 @@ def test_one_hot_values_expose_p():
 
 
 @pytest.mark.parametrize("d", [64, 128])
+def test_wide_scores_every_tile_shape(d):
+    # the sigma-4 scores of the test above (many jumps of the running max, so the rescale and its
+    # wave-uniform skip both run) through every tile shape of the table, on a ragged length
+    shapes = {64: [(128, 64, 4), (128, 128, 4), (64, 64, 2), (128, 64, 2), (256, 64, 4), (256, 64, 8),
+                   (64, 64, 4)],
+              128: [(128, 64, 4), (64, 64, 2)]}[d]
+    qb, kb, _ = make_qkv(1, 3, 777, d, seed=50 + d, sigma=4.0)
+    _, _, vb = make_qkv(1, 3, 777, d, seed=51 + d)
+    scale = 1.0 / math.sqrt(d)
+    for causal in (True, False):
+        o_ref, lse_ref = oracle.attention_fwd(qb, kb, vb, causal, scale)
+        for bm, bn, w in shapes:
+            say(f"[gpu] sigma4 tile {bm}x{bn} waves={w} d={d} causal={causal}")
+            o, lse = run_gpu_ex(qb, kb, vb, causal, scale, bm, bn, w)
+            assert_parity(compare(o, lse, o_ref, lse_ref), f"sigma4 tile {bm}x{bn}x{w} d={d}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_every_tile_shape(d):
     from exact_tiled_attention_07_amd.fa import lib  # noqa: F401  (library must be loaded)
     shapes = {64: [(128, 64, 4), (128, 128, 4), (64, 64, 2), (128, 64, 2), (256, 64, 4), (256, 64, 8),
