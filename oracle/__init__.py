@@ -32,7 +32,8 @@ sequence (one library matmul per head for the scores and one for P V), and ``att
 the backward's definitions evaluated for selected query and key rows of long heads.
 
 ``attention_fwd_fp8`` decodes FP8 E4M3 codes exactly, applies the per-tensor descale factors in
-float64 and calls the float64 forward.
+float64 and calls the float64 forward; ``attention_fwd_fp8_rows`` evaluates the same definition in
+numpy for selected rows of long heads.
 
 Every function here is pinned by the ``not gpu`` tests in ``tests/test_oracle_pins.py``,
 ``tests/test_oracle_bwd_pins.py``, ``tests/test_oracle_sparse_pins.py``,
@@ -448,3 +449,28 @@ def attention_fwd_fp8(q8, k8, v8, causal: bool, scale: float, q_descale: float, 
     k = e4m3_to_f64(k8) * kd
     v = e4m3_to_f64(v8) * vd
     return attention_fwd_f64(q, k, v, causal, scale, num_threads)
+
+
+def attention_fwd_fp8_rows(q8, k8, v8, causal: bool, scale: float, q_descale: float, k_descale: float,
+                           v_descale: float, rows):
+    """``attention_fwd_fp8`` for selected rows only (numpy float64), for heads too long for the
+    whole-head entry. ``rows`` holds ``(b, h, i)`` triples; returns ``(o, lse)`` with ``o``
+    ``[len(rows), d]`` and ``lse`` ``[len(rows)]``. Each row is the same two-pass softmax over its
+    visible keys (j <= i when causal) of the decoded, descaled values."""
+    qd, kd, vd = (float(np.float32(s)) for s in (q_descale, k_descale, v_descale))
+    d = np.asarray(q8).shape[-1]
+    o, lse = np.empty((len(rows), d)), np.empty(len(rows))
+    heads = {}
+    for n, (b, h, i) in enumerate(rows):
+        if (b, h) not in heads:
+            heads[(b, h)] = (e4m3_to_f64(q8[b, h]) * qd, e4m3_to_f64(k8[b, h]) * kd,
+                             e4m3_to_f64(v8[b, h]) * vd)
+        q, k, v = heads[(b, h)]
+        keys = i + 1 if causal else k.shape[0]
+        s = scale * (k[:keys] @ q[i])
+        m = s.max()
+        e = np.exp(s - m)
+        l = e.sum()
+        o[n] = (e @ v[:keys]) / l
+        lse[n] = m + np.log(l)
+    return o, lse

@@ -91,25 +91,12 @@ def check(q8, k8, v8, scales, causal, scale, label, rows=None):
         o_ref = o_ref.reshape(-1, d)
         lse_ref = lse_ref.reshape(-1)
     else:
-        # oracle on whole heads only where needed: the rows' heads, by the row-wise numpy model below
-        o_ref = None
+        o_ref = None  # the oracle's row entry, below
     bound, lbound, pred = error_model(q8, k8, v8, scales, causal, scale, rows)
     got_o = np.stack([o[b, h, i] for b, h, i in rows])
     got_l = np.array([lse[b, h, i] for b, h, i in rows])
     if o_ref is None:
-        sub = {}
-        for b, h, i in rows:
-            sub.setdefault((b, h), []).append(i)
-        ref_o, ref_l = [], []
-        for (b, h), idx in sub.items():
-            oo, ll = oracle.attention_fwd_fp8(q8[b:b + 1, h:h + 1], k8[b:b + 1, h:h + 1], v8[b:b + 1, h:h + 1],
-                                              causal, scale, *scales)
-            for i in idx:
-                ref_o.append(oo[0, 0, i]); ref_l.append(ll[0, 0, i])
-        order = [(b, h, i) for (b, h), idx in sub.items() for i in idx]
-        pos = {r: n for n, r in enumerate(order)}
-        o_ref = np.stack([ref_o[pos[r]] for r in rows])
-        lse_ref = np.array([ref_l[pos[r]] for r in rows])
+        o_ref, lse_ref = oracle.attention_fwd_fp8_rows(q8, k8, v8, causal, scale, *scales, rows)
     err = np.abs(got_o - o_ref)
     lerr = np.abs(got_l - lse_ref)
     mse, pmse = float((err ** 2).mean()), float(pred.mean())
@@ -145,10 +132,17 @@ def test_fp8_full_size_sampled_rows(name):
                                                       rng.integers(0, wl.T, 40))]
     rows += [(0, 0, 0), (0, 0, 63), (0, 0, 64), (wl.B - 1, wl.H - 1, wl.T - 1), (1, 2, 4095)]
     rows = sorted(set(rows))
-    # the oracle runs on whole heads; keep the number of distinct heads small
-    heads = sorted({(b, h) for b, h, _ in rows})[:6]
-    rows = [r for r in rows if (r[0], r[1]) in heads]
     check(q8, k8, v8, scales, wl.causal, wl.scale, wl.name + " fp8 sampled", rows=rows)
+
+
+def test_fp8_long_head_sampled_rows():
+    # one head of 2^18 queries and keys (the last Q block walks 4096 K/V tiles), causal, sampled rows
+    T = 1 << 18
+    q8, k8, v8, scales = make_qkv_fp8(1, 1, T, 64, seed=18, sigma=2.0)
+    rng = np.random.default_rng(18)
+    rows = sorted({(0, 0, int(i)) for i in [0, 1, 63, 64, 127, 128, T // 2, T - 2, T - 1]
+                   + rng.integers(0, T, 20).tolist()})
+    check(q8, k8, v8, scales, True, 0.125, "T=2^18 fp8 sampled", rows=rows)
 
 
 def test_fp8_scales_and_descales():

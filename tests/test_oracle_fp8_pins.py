@@ -8,6 +8,7 @@ F4 power-of-two descales: q and k descales act as a factor on the scale, the v d
    O only (exact identities in binary floating point).
 F5 the generator's quantization: round to nearest (the nearest code, found by brute force over the
    decoded table, with ties to the even code), amax maps to 448, per-tensor descale amax / 448.
+F6 the row entry for long heads (numpy) equals the whole-head FP8 oracle on every row.
 """
 import numpy as np
 import pytest
@@ -73,3 +74,15 @@ def test_f5_quantization_is_round_to_nearest():
     for c, s in zip((q8, k8, v8), scales):
         assert np.abs(oracle.e4m3_to_f64(c)).max() == 448.0
         assert s == float(np.float32(s))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_f6_row_entry_matches_the_whole_head_oracle(causal):
+    # attention_fwd_fp8_rows (numpy, rows) against attention_fwd_fp8 (the C float64 forward on the
+    # decoded values, pinned by F1-F5) on every row of small heads
+    q8, k8, v8, sc = make_qkv_fp8(2, 2, 150, 64, seed=71, sigma=2.0)
+    o, lse = oracle.attention_fwd_fp8(q8, k8, v8, causal, 0.125, *sc)
+    rows = [(b, h, i) for b in range(2) for h in range(2) for i in range(150)]
+    ro, rl = oracle.attention_fwd_fp8_rows(q8, k8, v8, causal, 0.125, *sc, rows)
+    np.testing.assert_allclose(ro, o.reshape(-1, 64), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(rl, lse.reshape(-1), rtol=1e-12, atol=1e-12)
