@@ -47,9 +47,11 @@ def fill(dst_tensors, B, H, T, d, seed):
 
 
 @pytest.mark.parametrize("B,H,T,d,causal", [(2, 3, 1000, 64, True), (1, 2, 300, 128, False),
-                                            (1, 2, 40, 64, True)])
+                                            (1, 2, 40, 64, True), (4, 12, 1024, 64, True)])
 def test_fwd_graph_replays(B, H, T, d, causal):
-    # the last shape takes the key-split launch
+    # the default launch of each shape: the key split, 128 x 64 (d = 128), 128 x 64, 128 x 128
+    assert d == 128 or [fa.plan(B, H, T, d, causal)[x] for x in ("key_split", "block_n")] == {
+        1000: [2, 64], 40: [1, 64], 1024: [1, 128]}[T]
     q, k, v = (torch.empty(B, H, T, d, dtype=torch.bfloat16, device=DEV) for _ in range(3))
     o = torch.empty_like(q)
     lse = torch.empty(B, H, T, dtype=torch.float32, device=DEV)
@@ -123,3 +125,30 @@ def test_bwd_graph_replays(d):
         torch.cuda.synchronize()
         for name, a, b in zip(("dq", "dk", "dv", "delta"), (dq, dk, dv, delta), got):
             assert_same(a, b, f"{name}, replay {r}")
+
+
+def test_fp8_graph_replays():
+    from exact_tiled_attention_07_amd.inputs import make_qkv_fp8
+    B, H, T, d = 2, 2, 900, 64
+    q, k, v = (torch.empty(B, H, T, d, dtype=torch.uint8, device=DEV) for _ in range(3))
+    o = torch.empty(B, H, T, d, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(B, H, T, dtype=torch.float32, device=DEV)
+
+    def refill(seed):
+        q8, k8, v8, sc = make_qkv_fp8(B, H, T, d, seed=seed)
+        for dst, src in zip((q, k, v), (q8, k8, v8)):
+            dst.copy_(torch.from_numpy(src).to(DEV))
+        return sc
+
+    sc = refill(7)
+    # the descale factors are launch arguments, fixed at capture: replays reuse the captured ones
+    g = capture(lambda: fa.fwd_fp8(q, k, v, *sc, causal=True, out=o, lse=lse))
+    for r in range(REPLAYS):
+        refill(700 + r)
+        o.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        o_e, lse_e = fa.fwd_fp8(q, k, v, *sc, causal=True)
+        torch.cuda.synchronize()
+        assert_same(o, o_e, f"o, replay {r}")
+        assert_same(lse, lse_e, f"lse, replay {r}")
