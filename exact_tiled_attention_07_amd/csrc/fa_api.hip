@@ -103,6 +103,7 @@ const TileEntry kTiles[] = {
     entry<64, 1, 4, 64, 2, 2>(),  // d=64: 64 queries, two waves per 32 queries splitting the keys
     entry<128, 1, 4, 64>(),  // d=128: 128 queries (4 waves x 32), 64-key tiles
     entry<128, 1, 2, 64>(),  // d=128: 64 x 64
+    entry<128, 1, 8, 64>(),  // d=128: 256 queries (8 waves x 32), 64-key tiles
 };
 
 const TileEntry* find_tile(int d, int block_m, int block_n, int waves) {
@@ -132,7 +133,14 @@ bool take_wide_key_tiles(int64_t nq, int64_t grid) {
   return nq >= 5 && (nq <= 8 || grid <= 768);
 }
 
+// d = 128, non-causal, T >= 2048: 256 queries in 8 waves per workgroup share each K/V tile copied to
+// LDS (half the copies per query; 222 VGPRs, one workgroup of 8 waves per CU). Measured against
+// 128 x 64 x 4: 0.964-0.977 non-causal (B1-B4 H16, T = 4096 and 8192), 0.991-1.002 causal (kept).
 const TileEntry* default_tile(int d, int T, int64_t BH, bool causal) {
+  if (d == 128 && !causal && T >= 2048) {
+    const TileEntry* t = find_tile(128, 256, 64, 8);
+    if (t) return t;
+  }
   if (d == 64) {
     const int64_t nq = (T + 127) / 128, grid = nq * BH;
     const TileEntry* t = nullptr;

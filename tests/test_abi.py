@@ -153,8 +153,12 @@ def test_plan_default_tile_for_short_sequences():
     assert pick(1, 12, 1024, False) == "split"    # non-causal, grid 96
     assert pick(4, 12, 1024, False) == "128x128"  # non-causal, grid 384
     assert pick(4, 16, 8192, False) == "128x64"   # non-causal, grid 4096
-    assert fa.plan(1, 1, 8, 128, True)["key_split"] == 1      # d = 128: always 128 x 64
+    assert fa.plan(1, 1, 8, 128, True)["key_split"] == 1      # d = 128: 128 x 64 ...
     assert fa.plan(1, 1, 8, 128, True)["block_n"] == 64
+    assert fa.plan(4, 16, 8192, 128, True)["block_m"] == 128
+    p = fa.plan(4, 16, 8192, 128, False)                        # ... or, non-causal from T = 2048,
+    assert (p["block_m"], p["block_n"], p["waves"], p["grid"]) == (256, 64, 8, 32 * 64)  # 256 x 64 x 8
+    assert fa.plan(4, 16, 1024, 128, False)["block_m"] == 128
     assert fa.plan(4, 12, 4096, 64, True, 64, 64, 4)["key_split"] == 2  # forced
     assert fa.plan(1, 1, 8, 64, True, 128, 64, 4)["key_split"] == 1
 

@@ -240,7 +240,7 @@ def test_wide_scores_every_tile_shape(d):
     # wave-uniform skip both run) through every tile shape of the table, on a ragged length
     shapes = {64: [(128, 64, 4), (128, 128, 4), (64, 64, 2), (128, 64, 2), (256, 64, 4), (256, 64, 8),
                    (64, 64, 4)],
-              128: [(128, 64, 4), (64, 64, 2)]}[d]
+              128: [(128, 64, 4), (64, 64, 2), (256, 64, 8)]}[d]
     qb, kb, _ = make_qkv(1, 3, 777, d, seed=50 + d, sigma=4.0)
     _, _, vb = make_qkv(1, 3, 777, d, seed=51 + d)
     scale = 1.0 / math.sqrt(d)
@@ -257,7 +257,7 @@ def test_every_tile_shape(d):
     from exact_tiled_attention_07_amd.fa import lib  # noqa: F401  (library must be loaded)
     shapes = {64: [(128, 64, 4), (128, 128, 4), (64, 64, 2), (128, 64, 2), (256, 64, 4), (256, 64, 8),
                    (64, 64, 4)],
-              128: [(128, 64, 4), (64, 64, 2)]}[d]
+              128: [(128, 64, 4), (64, 64, 2), (256, 64, 8)]}[d]
     qb, kb, vb = make_qkv(2, 3, 1000, d, seed=31 + d)
     scale = 1.0 / math.sqrt(d)
     for causal in (True, False):
