@@ -1,14 +1,19 @@
 """Benchmark of the exact attention forward on one MI355X.
 
 A step is one fa_fwd call over the whole workload (all heads), inputs already resident in HBM.
-Prints one JSON line:
+Warm-up runs the given number of steps and then more until 0.3 s have passed (the shader clock rises
+over the first part of a load); exactly `--steps` steps are timed. Prints one JSON line:
   value        counted TFLOP/s of the step (2*B*H*T^2*d causal, 4*B*H*T^2*d non-causal)
-  roofline     the kernel's achieved TFLOP/s from per-launch HIP events on its own stream,
-               against the dense bf16 MFMA peak; traffic = HBM bytes per launch from rocprofv3
-               counters (when they were taken on the current kernel sources), else null; the same
-               holds for clock_mhz, the shader clock measured under the kernel, and the fraction
-               of the MFMA peak at that clock
+  roofline     the kernel's achieved TFLOP/s from one pair of HIP events on its launch stream
+               around the timed launches, against the dense bf16 MFMA peak; traffic = HBM bytes
+               per launch from rocprofv3 counters (when they were taken on the current kernel
+               sources), else null; the same holds for clock_mhz, the shader clock measured under
+               the kernel, and the fraction of the MFMA peak at that clock
   cpu_baseline the CPU oracle timed on the host cores on a bounded sample of the same workload
+               (per_config: the oracle on every workload, and on one thread for the smallest)
+  parity       the timed launch's output against that same oracle output, every row of the
+               sampled heads (all of them at T=4096): literal max errors, the number of elements
+               admitted only by the one-ulp clause, and the number of failures
   sweep        the same measurement at the other sequence lengths of the metric (T = 1024, 2048,
                8192, 16384) and on the d=128 workload (non-causal, and its causal variant)
   backward     fa_bwd (dQ, dK, dV from the forward's O and LSE) on the same workload: counted
@@ -121,8 +126,45 @@ def recorded_clock_mhz():
     return float(m_clk.group(1))
 
 
+MIN_WARM_S = 0.3  # warm-up spans at least this much wall time: the shader clock rises under load
+
+
+def warm_up(step, warmup, sync, min_s=MIN_WARM_S):
+    """Run `warmup` steps, then more in batches until at least `min_s` seconds have passed."""
+    t0 = time.perf_counter()
+    for _ in range(warmup):
+        step()
+    sync()
+    n = max(1, warmup)
+    while time.perf_counter() - t0 < min_s:
+        for _ in range(n):
+            step()
+        sync()
+        n = min(2 * n, 4096)
+
+
+def time_region(step, steps, stream, sync):
+    """Time exactly `steps` back-to-back launches: wall clock between two synchronisations, and one
+    pair of HIP events on the launch stream around the same launches. Returns (wall ms per step,
+    event ms per step); the event figure cannot exceed the wall figure by more than the events'
+    own resolution, as nothing but the launches sits between them."""
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    sync()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    sync()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    return wall_ms, e0.elapsed_time(e1) / steps
+
+
 def time_workload(wl, steps, warmup, tiles=None):
-    """Returns (ms_per_step wall, avg kernel ms from per-launch events, outputs)."""
+    """Returns (ms_per_step wall, kernel ms per launch from one event pair around the same timed
+    launches, extra stats, (o, lse) of the last launch on the device)."""
     import torch
 
     import exact_tiled_attention_07_amd as fa
@@ -142,25 +184,21 @@ def time_workload(wl, steps, warmup, tiles=None):
         else:
             fa.fwd_ex(q, k, v, *tiles, causal=wl.causal, scale=wl.scale, out=o, lse=lse, stream=stream)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize(dev)
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    def sync():
+        torch.cuda.synchronize(dev)
 
-    # per-launch kernel duration: an event pair around each launch, on the launch stream
+    warm_up(step, warmup, sync)
+    wall_ms, kern_ms = time_region(step, steps, stream, sync)
+
+    # per-launch event pairs (informational: the brackets themselves add a little time per launch)
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     for i in range(steps):
         starts[i].record(stream)
         step()
         ends[i].record(stream)
-    torch.cuda.synchronize(dev)
+    sync()
     durs = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    avg_ms = sum(durs) / len(durs)
 
     # one cold launch: flush L2/MALL by writing 512 MiB first
     scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -169,17 +207,20 @@ def time_workload(wl, steps, warmup, tiles=None):
     c0.record(stream)
     step()
     c1.record(stream)
-    torch.cuda.synchronize(dev)
+    sync()
     cold_ms = c0.elapsed_time(c1)
-    del scratch
-    return wall_ms, avg_ms, {"median_ms": durs[len(durs) // 2], "min_ms": durs[0], "max_ms": durs[-1],
-                             "cold_ms": cold_ms}
+    del scratch, q, k, v
+    return wall_ms, kern_ms, {"per_launch_events": {"median_ms": round(durs[len(durs) // 2], 5),
+                                                    "min_ms": round(durs[0], 5),
+                                                    "max_ms": round(durs[-1], 5)},
+                              "cold_ms": round(cold_ms, 5)}, (o, lse)
 
 
 def time_backward(wl, steps, warmup):
     """fa_bwd on the workload's inputs (o and lse from one fa_fwd, dO drawn like the inputs).
 
-    Returns (avg ms per fa_bwd call from per-launch events on the launch stream, extra stats)."""
+    Returns (ms per fa_bwd call from one event pair on the launch stream around the timed calls,
+    extra stats)."""
     import torch
 
     import exact_tiled_attention_07_amd as fa
@@ -197,24 +238,12 @@ def time_backward(wl, steps, warmup):
         fa.bwd(q, k, v, o, lse, do, causal=wl.causal, scale=wl.scale, dq=dq, dk=dk, dv=dv,
                delta=delta, stream=stream)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize(dev)
-    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    for i in range(steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize(dev)
-    durs = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
-    return sum(durs) / len(durs), {"wall_ms": wall_ms, "median_ms": durs[len(durs) // 2],
-                                    "min_ms": durs[0], "max_ms": durs[-1]}
+    def sync():
+        torch.cuda.synchronize(dev)
+
+    warm_up(step, warmup, sync)
+    wall_ms, ev_ms = time_region(step, steps, stream, sync)
+    return ev_ms, {"wall_ms": wall_ms}
 
 
 def sparse_mask(T, density, seed):
@@ -261,18 +290,7 @@ def time_sparse(wl, steps, warmup, density=0.25):
     o, lse = torch.empty_like(q), torch.empty((wl.B, wl.H, wl.T), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    def timed(fn):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize(dev)
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        for i in range(steps):
-            starts[i].record(stream)
-            fn()
-            ends[i].record(stream)
-        torch.cuda.synchronize(dev)
-        return sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / steps
+    timed = _event_timer(stream, steps, warmup)
 
     ms_sparse = timed(lambda: fa.fwd_sparse(q, k, v, mask, causal=wl.causal, scale=wl.scale, out=o,
                                             lse=lse, stream=stream))
@@ -289,20 +307,16 @@ def time_sparse(wl, steps, warmup, density=0.25):
 
 
 def _event_timer(stream, steps, warmup):
+    """A timer for one entry point: time-based warm-up, then ms per call from one event pair around
+    `steps` back-to-back calls on the launch stream."""
     import torch
 
+    def sync():
+        torch.cuda.synchronize(stream.device)
+
     def timed(fn):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize(stream.device)
-        starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-        for i in range(steps):
-            starts[i].record(stream)
-            fn()
-            ends[i].record(stream)
-        torch.cuda.synchronize(stream.device)
-        return sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / steps
+        warm_up(fn, warmup, sync, min_s=0.1)
+        return time_region(fn, steps, stream, sync)[1]
     return timed
 
 
@@ -417,20 +431,25 @@ def time_fp8(names, steps, warmup):
     return out
 
 
-def cpu_baseline(wl, budget_s=20.0):
-    """Time the CPU oracle on a bounded sample of the workload (whole heads, all host cores)."""
+def _oracle_flops(wl, T, rows_per_head, heads):
+    """Counted flops (the metric's count) of `heads` heads, `rows_per_head` rows each."""
     import numpy as np
 
+    i = np.arange(rows_per_head, dtype=np.float64)
+    per_head = (4.0 * wl.d * (i + 1)).sum() if wl.causal else 4.0 * wl.d * T * rows_per_head
+    return float(per_head * heads)
+
+
+def cpu_baseline(wl, budget_s=20.0):
+    """Time the CPU oracle on a bounded sample of the workload (whole heads, all host cores).
+
+    Returns (the bench line's cpu_baseline object, oracle (o, lse) of the sampled heads, the number
+    of sampled heads): the same oracle output is the reference of the bench's parity check."""
     import oracle
 
     threads = len(os.sched_getaffinity(0))
     qb, kb, vb = wl.make()
     d, T = wl.d, wl.T
-
-    def counted_flops(rows_per_head, heads):
-        i = np.arange(rows_per_head, dtype=np.float64)
-        per_head = (4.0 * d * (i + 1)).sum() if wl.causal else 4.0 * d * T * rows_per_head
-        return per_head * heads
 
     # probe with one head, then take as many whole heads as fit the time budget
     t0 = time.perf_counter()
@@ -440,13 +459,66 @@ def cpu_baseline(wl, budget_s=20.0):
     n_heads = max(1, min(n_heads_total, int(budget_s / max(probe_s, 1e-6))))
     flat = [x.reshape(1, n_heads_total, T, d)[:, :n_heads] for x in (qb, kb, vb)]
     t0 = time.perf_counter()
-    oracle.attention_fwd(*flat, wl.causal, wl.scale, num_threads=threads)
+    o_ref, lse_ref = oracle.attention_fwd(*flat, wl.causal, wl.scale, num_threads=threads)
     dt = time.perf_counter() - t0
-    fl = counted_flops(T, n_heads)
-    return {"value": float(fl / dt / 1e12), "unit": "TFLOP/s", "cores": oracle.threads_used(threads),
+    fl = _oracle_flops(wl, T, T, n_heads)
+    base = {"value": float(fl / dt / 1e12), "unit": "TFLOP/s", "cores": oracle.threads_used(threads),
             "kind": "oracle",
             "sample": f"{n_heads} of {n_heads_total} heads of {wl.name} (all {T} rows each), "
                       f"fp64 two-pass oracle, {dt:.1f} s"}
+    return base, (o_ref, lse_ref), n_heads
+
+
+def cpu_baseline_per_config(budget_heads_s=3.0):
+    """The oracle timed on every workload: C1-C4 whole (C1 also on one thread); C5a and C5b on whole
+    heads of their shape (seeded N(0,1) draws of those heads), as many as fit about `budget_heads_s`
+    seconds. The oracle's time does not depend on the values."""
+    import oracle
+    from exact_tiled_attention_07_amd.inputs import WORKLOADS, make_qkv
+
+    threads = len(os.sched_getaffinity(0))
+    out = {}
+    for name in ("c1", "c2", "c3", "c4", "c5a", "c5b"):
+        wl = WORKLOADS[name]
+        for nt in ((threads, 1) if name == "c1" else (threads,)):
+            if name in ("c5a", "c5b"):
+                q1, k1, v1 = make_qkv(1, 1, wl.T, wl.d, seed=wl.seed + 1000)
+                t0 = time.perf_counter()
+                oracle.attention_fwd(q1, k1, v1, wl.causal, wl.scale, num_threads=nt)
+                probe = time.perf_counter() - t0
+                heads = max(1, min(wl.B * wl.H, int(budget_heads_s / max(probe, 1e-6))))
+                qb, kb, vb = make_qkv(1, heads, wl.T, wl.d, seed=wl.seed + 1000)
+                sample = f"{heads} of {wl.B * wl.H} heads of the {wl.name} shape (all rows)"
+            else:
+                qb, kb, vb = wl.make()
+                heads = wl.B * wl.H
+                sample = f"all of {wl.name}"
+            t0 = time.perf_counter()
+            oracle.attention_fwd(qb, kb, vb, wl.causal, wl.scale, num_threads=nt)
+            dt = time.perf_counter() - t0
+            fl = _oracle_flops(wl, wl.T, wl.T, heads)
+            key = name if nt == threads else f"{name}_1thread"
+            out[key] = {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s",
+                        "cores": oracle.threads_used(nt), "kind": "oracle", "seconds": round(dt, 3),
+                        "sample": sample}
+    return out
+
+
+def parity_check(wl, o, lse, ref, n_heads):
+    """The timed launch's output against the oracle output of the cpu_baseline leg (same inputs),
+    over the heads the oracle computed, every row; the pages' tolerance (oracle/parity.py)."""
+    from oracle.parity import compare, passed
+
+    o_ref, lse_ref = ref
+    BH = wl.B * wl.H
+    og = o.reshape(BH, wl.T, wl.d)[:n_heads].float().cpu().numpy().reshape(o_ref.shape)
+    lg = lse.reshape(BH, wl.T)[:n_heads].cpu().numpy().reshape(lse_ref.shape)
+    st = compare(og, lg, o_ref, lse_ref)
+    return {"workload": wl.name, "heads": n_heads, "rows": n_heads * wl.T, "elements": st["n"],
+            "max_err_o": st["max_err_o"], "max_err_lse": st["max_err_lse"],
+            "n_ulp_clause": st["n_ulp_clause"], "n_fail": st["n_fail_o"] + st["n_fail_lse"] + st["n_nonfinite"],
+            "pass": passed(st),
+            "tolerance": "|dO| <= 1.5e-2, or one bf16 ulp where |O_ref| >= 2; |dLSE| <= 1e-3"}
 
 
 def copy_calibration(mib):
@@ -525,7 +597,7 @@ def main(argv=None):
             copy_calibration(args.copy_calibration_mib)
             print(json.dumps({"backward": backward}), flush=True)
             return 0
-    wall_ms, kern_ms, extra = time_workload(wl, args.steps, args.warmup, tiles)
+    wall_ms, kern_ms, extra, (o_dev, lse_dev) = time_workload(wl, args.steps, args.warmup, tiles)
     value = wl.flops / (wall_ms * 1e-3) / 1e12
     achieved = wl.flops / (kern_ms * 1e-3) / 1e12
     print(f"[bench] {wl.name}: {wall_ms:.4f} ms/step, kernel {kern_ms:.4f} ms, {value:.1f} TFLOP/s",
@@ -549,7 +621,7 @@ def main(argv=None):
             est_s = w2.flops / 800e12
             n_t = min(2000, max(5, args.steps // 5, math.ceil(0.025 / est_s)))
             n_w = min(2000, max(2, args.warmup // 5, math.ceil(0.025 / est_s)))
-            wms, kms, ex2 = time_workload(w2, n_t, n_w, None)
+            wms, kms, ex2, _ = time_workload(w2, n_t, n_w, None)
             sweep[name] = {"workload": w2.name, "ms_per_step": round(wms, 5),
                            "tflops": round(w2.flops / (wms * 1e-3) / 1e12, 2),
                            "kernel_tflops": round(w2.flops / (kms * 1e-3) / 1e12, 2),
@@ -573,10 +645,15 @@ def main(argv=None):
 
     copy_calibration(args.copy_calibration_mib)
 
-    base = None
+    base = parity = None
     if not args.no_cpu_baseline:
-        base = cpu_baseline(wl)
+        base, ref, n_heads = cpu_baseline(wl)
         print(f"[bench] cpu baseline: {base}", file=sys.stderr, flush=True)
+        parity = parity_check(wl, o_dev, lse_dev, ref, n_heads)
+        print(f"[bench] parity: {parity}", file=sys.stderr, flush=True)
+        del ref
+        base["per_config"] = cpu_baseline_per_config()
+        print(f"[bench] cpu baseline per config: {base['per_config']}", file=sys.stderr, flush=True)
 
     profiled = args.workload == PROFILED_WORKLOAD and tiles is None
     traffic = recorded_traffic() if profiled else None
@@ -605,8 +682,11 @@ def main(argv=None):
                      "clock_mhz": clock,
                      "peak_at_clock": round(peak_at_clock, 1) if peak_at_clock else None,
                      "frac_at_clock": round(achieved / peak_at_clock, 4) if peak_at_clock else None,
-                     "flops_per_launch": wl.flops, **{k: round(v, 5) for k, v in extra.items()}},
+                     "timing": "achieved = flops per launch / (one HIP event pair on the launch stream "
+                               "around the timed launches / steps)",
+                     "flops_per_launch": wl.flops, **extra},
         "cpu_baseline": base,
+        "parity": parity,
         "sweep": sweep,
         "backward": backward,
         "sparse": sparse,

@@ -10,3 +10,19 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """List the recorded parity statistics (literal max errors, elements admitted only by the
+    one-ulp clause) at the end of the run, so that they survive a quiet (-q) run's output."""
+    try:
+        from parity import RECORDED
+    except ImportError:
+        return
+    if not RECORDED:
+        return
+    terminalreporter.section("parity against the oracle (rows compared in full)")
+    for label, s in RECORDED:
+        terminalreporter.write_line(
+            f"{label}: n={s['n']} max|dO|={s['max_err_o']:.4e} max|dLSE|={s['max_err_lse']:.3e} "
+            f"ulp_clause={s['n_ulp_clause']} fail={s['n_fail_o'] + s['n_fail_lse']}")

@@ -1,43 +1,20 @@
 """Comparison of GPU outputs with the CPU oracle (test helper; no attention arithmetic).
 
-Tolerance on O (bf16): an element passes when |O_gpu - O_ref| <= 1.5e-2, or, where |O_ref| >= 2,
-when it is within one bf16 ulp of O_ref. The second clause exists because at |O| >= 4 the bf16
-spacing is 2^-5, so even the correctly rounded exact answer can sit 1.5625e-2 away from it; the
-clause admits exactly the two bf16 neighbours of the exact value (and nothing farther). The
-literal max error and the number of elements that needed the ulp clause are reported.
-Tolerance on LSE (fp32): |LSE_gpu - LSE_ref| <= 1e-3.
+The tolerance itself lives in ``oracle/parity.py`` (shared with the bench's parity check): an O
+element passes when |O_gpu - O_ref| <= 1.5e-2, or, where |O_ref| >= 2, when it is within one bf16
+ulp of O_ref; LSE passes when |LSE_gpu - LSE_ref| <= 1e-3. ``record`` keeps the statistics of
+named checks so that the end of a pytest run can print them (``conftest.py``).
 """
 from __future__ import annotations
 
-import numpy as np
+from oracle.parity import LSE_TOL, O_TOL, bf16_ulp, compare, passed  # noqa: F401
 
-O_TOL = 1.5e-2
-LSE_TOL = 1e-3
-
-
-def bf16_ulp(x: np.ndarray) -> np.ndarray:
-    """Spacing of bf16 numbers at |x| (normal range): 2^(floor(log2|x|) - 7)."""
-    a = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), 2.0 ** -126)
-    return np.exp2(np.floor(np.log2(a)) - 7)
+# (label, stats) of the checks that asked to be listed in the run's summary
+RECORDED: list = []
 
 
-def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: np.ndarray) -> dict:
-    o_gpu = np.asarray(o_gpu, dtype=np.float64)
-    lse_gpu = np.asarray(lse_gpu, dtype=np.float64)
-    err = np.abs(o_gpu - o_ref)
-    literal_ok = err <= O_TOL
-    ulp_ok = (np.abs(o_ref) >= 2.0) & (err <= bf16_ulp(o_ref))
-    ok = literal_ok | ulp_ok
-    lerr = np.abs(lse_gpu - lse_ref)
-    return {
-        "max_err_o": float(err.max()) if err.size else 0.0,
-        "max_err_lse": float(lerr.max()) if lerr.size else 0.0,
-        "n_ulp_clause": int(np.count_nonzero(ok & ~literal_ok)),
-        "n_fail_o": int(np.count_nonzero(~ok)),
-        "n_fail_lse": int(np.count_nonzero(~(lerr <= LSE_TOL))),
-        "n_nonfinite": int(np.count_nonzero(~np.isfinite(o_gpu)) + np.count_nonzero(~np.isfinite(lse_gpu))),
-        "n": int(err.size),
-    }
+def record(label: str, stats: dict) -> None:
+    RECORDED.append((label, dict(stats)))
 
 
 def assert_parity(stats: dict, label: str = ""):
