@@ -5,8 +5,10 @@ The work runs in hand-written gfx950 HIP kernels behind the C-ABI library ``libf
 (``include/fa.h``); this package is its thin Python binding. PyTorch provides device memory and
 streams only.
 """
-from .fa import (FaError, bwd, fwd, fwd_ex, fwd_fp8, fwd_partial, fwd_sparse, fwd_splitkv, merge,
-                 plan, sparse_mask_shape, splitkv_splits, splitkv_workspace_bytes, strerror)
+from .fa import (FaError, bwd, fwd, fwd_ex, fwd_fp8, fwd_partial, fwd_sparse, fwd_splitkv,
+                 fwd_splitkv_noalloc, merge, plan, sparse_mask_shape, splitkv_splits,
+                 splitkv_workspace_bytes, strerror)
 
-__all__ = ["FaError", "bwd", "fwd", "fwd_ex", "fwd_fp8", "fwd_partial", "fwd_sparse", "fwd_splitkv", "merge",
-           "plan", "sparse_mask_shape", "splitkv_splits", "splitkv_workspace_bytes", "strerror"]
+__all__ = ["FaError", "bwd", "fwd", "fwd_ex", "fwd_fp8", "fwd_partial", "fwd_sparse", "fwd_splitkv",
+           "fwd_splitkv_noalloc", "merge", "plan", "sparse_mask_shape", "splitkv_splits",
+           "splitkv_workspace_bytes", "strerror"]

@@ -3,8 +3,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <tuple>
 
 #include "fa.h"
@@ -12,6 +14,12 @@
 #include "fa_fp8_kernel.hpp"
 #include "fa_kernel.hpp"
 #include "fa_merge_kernel.hpp"
+
+// Fixed device buffer of fa_fwd_splitkv_noalloc: the fp32 partial results of the key ranges, for
+// callers that cannot allocate. Every GPU the library runs on holds its own copy until the process
+// ends. In host code `scratch` names a host-side stand-in, not device memory: its device address on
+// the current GPU comes from hipGetSymbolAddress, looked up once per device (scratch_address below).
+static __device__ __align__(256) char scratch[FA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -399,6 +407,48 @@ int launch_splitkv(const void* q, const void* k, const void* v, void* o, float* 
   return launch_merge_kernel(o_parts, lse_parts, used, o, lse, rows, d, stream);
 }
 
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kMaxDevices];  // per device; null until looked up
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the calling thread's current device.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FA_ERR_HIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FA_OK;
+}
+
+int launch_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                           int H, int T, int Tk, int d, int causal, float scale, int n_splits,
+                           void* stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (n_splits < 1 || n_splits > FA_MERGE_MAX_PARTS) return FA_ERR_INVALID_ARG;
+  int rc = check_sizes(B, H, T, d);
+  if (rc != FA_OK) return rc;
+  if (Tk < 0 || Tk > FA_MAX_T) return FA_ERR_INVALID_ARG;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) || ((uintptr_t)lse & 3u))
+    return FA_ERR_ALIGNMENT;
+  if ((size_t)B * H * T == 0) return FA_OK;  // an empty problem: nothing launched, no scratch used
+  const size_t need = fa_splitkv_workspace_bytes(B, H, T, d, n_splits);
+  if (need == 0 || need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != FA_OK) return rc;
+  return launch_splitkv(q, k, v, o, lse, B, H, T, Tk, d, causal, scale, n_splits, ws,
+                        FA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 // FP8 forward: E4M3 inputs with per-tensor descale factors, 128 queries x 64 keys per tile.
 int launch_fp8(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int T,
                int d, int causal, float scale, float q_descale, float k_descale, float v_descale,
@@ -546,6 +596,12 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* 
                         workspace_bytes, stream);
 }
 
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                           int H, int T, int Tk, int d, int causal, float scale, int n_splits,
+                           void* stream) {
+  return launch_splitkv_noalloc(q, k, v, o, lse, B, H, T, Tk, d, causal, scale, n_splits, stream);
+}
+
 int fa_merge(const float* o_parts, const float* lse_parts, int n_parts, void* o, float* lse, int B,
              int H, int T, int d, void* stream) {
   return launch_merge(o_parts, lse_parts, n_parts, o, lse, B, H, T, d, stream);
@@ -611,6 +667,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_ALIGNMENT: return "misaligned pointer (bf16 tensors need 16 bytes; lse and delta need 4)";
     case FA_ERR_HIP: return "HIP runtime error at kernel launch";
     case FA_ERR_TILE: return "tile shape not in the supported table";
+    case FA_ERR_SCRATCH: return "problem needs more scratch than the fixed no-allocation buffer holds (FA_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

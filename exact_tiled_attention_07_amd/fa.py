@@ -23,6 +23,7 @@ FA_ERR_UNSUPPORTED_D = -3
 FA_ERR_ALIGNMENT = -4
 FA_ERR_HIP = -5
 FA_ERR_TILE = -6
+FA_ERR_SCRATCH = -7
 
 _lib = None
 
@@ -79,6 +80,8 @@ def lib():
     L.fa_splitkv_splits.restype = ctypes.c_int
     L.fa_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp, ctypes.c_size_t, vp]
     L.fa_fwd_splitkv.restype = ctypes.c_int
+    L.fa_fwd_splitkv_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    L.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
     L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, f, f, f, vp]
     L.fa_fwd_fp8.restype = ctypes.c_int
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
@@ -371,6 +374,27 @@ def fwd_splitkv(q, k, v, causal: bool = True, scale: float | None = None, n_spli
                                     lse.data_ptr(), B, H, T, Tk, d, int(bool(causal)), scale, n_splits,
                                     workspace.data_ptr(), workspace.numel(),
                                     _stream_handle(q.device, stream)))
+    return out, lse
+
+
+def fwd_splitkv_noalloc(q, k, v, causal: bool = True, scale: float | None = None,
+                        n_splits: int | None = None, out=None, lse=None, stream=None):
+    """``fa_fwd_splitkv_noalloc``: split-KV attention whose partial results go through the library's
+    fixed device buffer (no workspace, no allocation by the library). Returns bf16 ``o`` and float32
+    ``lse``; pass ``out`` and ``lse`` to keep this call free of allocations too.
+    """
+    import torch
+
+    _check_inputs(q, k, v, keys_may_differ=True)
+    B, H, T, d = q.shape
+    Tk = k.shape[2]
+    out, lse = _outputs(q, out, lse)
+    n_splits = splitkv_splits(B, H, T, Tk, d) if n_splits is None else int(n_splits)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    with torch.cuda.device(q.device):
+        _check(lib().fa_fwd_splitkv_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                            lse.data_ptr(), B, H, T, Tk, d, int(bool(causal)), scale,
+                                            n_splits, _stream_handle(q.device, stream)))
     return out, lse
 
 

@@ -50,7 +50,9 @@ typedef enum fa_status {
   FA_ERR_ALIGNMENT = -4,      /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   FA_ERR_HIP = -5,            /* the kernel launch itself failed (its own status, not an earlier
                                  error still pending in hipGetLastError) */
-  FA_ERR_TILE = -6            /* fa_fwd_ex / fa_fwd_plan: tile shape not in the supported table */
+  FA_ERR_TILE = -6,           /* fa_fwd_ex / fa_fwd_plan: tile shape not in the supported table */
+  FA_ERR_SCRATCH = -7         /* fa_fwd_splitkv_noalloc: the problem needs more scratch than the
+                                 library's fixed buffer holds (FA_NOALLOC_SCRATCH_BYTES) */
 } fa_status;
 
 /* Largest accepted sequence length and largest accepted B*H (checked by every entry point). */
@@ -209,6 +211,28 @@ int fa_splitkv_splits(int B, int H, int T, int Tk, int d);
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                    int T, int Tk, int d, int causal, float scale, int n_splits, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/*
+ * fa_fwd_splitkv_noalloc — fa_fwd_splitkv without a workspace argument and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). The fp32 partial results go through a fixed buffer that the
+ * library holds in device memory, FA_NOALLOC_SCRATCH_BYTES per GPU, from the first call on that GPU
+ * until the process ends.
+ *   q, k, v, o, lse, B, H, T, Tk, d, causal, scale, n_splits, stream  as for fa_fwd_splitkv; the
+ *            scratch used is that of the calling thread's current device, so `stream` must belong
+ *            to that device
+ * Needs fa_splitkv_workspace_bytes(B, H, T, d, n_splits) <= FA_NOALLOC_SCRATCH_BYTES, else returns
+ * FA_ERR_SCRATCH before anything is launched (a smaller n_splits needs less). The first call on a
+ * device looks up the buffer's device address (FA_ERR_HIP if that fails); no call allocates, frees,
+ * copies or clears memory: every partial result the merge reads is written first by the same call.
+ * All calls on one GPU share its buffer, so calls that overlap in time on one GPU (two streams, or
+ * two host threads) race and give undefined results; calls ordered on one stream are safe.
+ * Results are bit-identical to fa_fwd_splitkv with the same n_splits.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                           int H, int T, int Tk, int d, int causal, float scale, int n_splits,
+                           void* stream);
 
 /*
  * fa_fwd_fp8 — the attention forward on FP8 inputs: q, k and v are OCP FP8 E4M3 codes ("e4m3fn":

@@ -22,8 +22,8 @@ def call(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A, B=1, H=1, T=8, d=64, causal=
 def test_library_exports_every_declared_function():
     names = fa.header_functions()
     assert names == ["fa_bwd", "fa_fwd", "fa_fwd_ex", "fa_fwd_fp8", "fa_fwd_partial", "fa_fwd_plan",
-                     "fa_fwd_sparse", "fa_fwd_splitkv", "fa_merge", "fa_splitkv_splits",
-                     "fa_splitkv_workspace_bytes", "fa_strerror"]
+                     "fa_fwd_sparse", "fa_fwd_splitkv", "fa_fwd_splitkv_noalloc", "fa_merge",
+                     "fa_splitkv_splits", "fa_splitkv_workspace_bytes", "fa_strerror"]
     lib = fa.lib()
     for n in names:
         assert hasattr(lib, n)
@@ -101,11 +101,11 @@ def test_fwd_ex_tile_checks():
 
 def test_strerror_covers_codes():
     seen = set()
-    for code in range(-6, 1):
+    for code in range(-7, 1):
         s = fa.strerror(code)
         assert s and s != "unknown status"
         seen.add(s)
-    assert len(seen) == 7
+    assert len(seen) == 8
     assert fa.strerror(-99) == "unknown status"
 
 
@@ -349,3 +349,45 @@ def test_fp8_checks():
     assert call_fp8(k=2 * A + 8) == fa.FA_ERR_ALIGNMENT
     assert call_fp8(lse=12 * A + 2) == fa.FA_ERR_ALIGNMENT
     assert call_fp8(o=A + 64) == fa.FA_ERR_INVALID_ARG             # output over q
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # include/fa.h: FA_NOALLOC_SCRATCH_BYTES
+
+
+def call_noalloc(B=1, H=2, T=4, Tk=1000, d=64, n=4, scale=0.125, **kw):
+    p = dict(q=A, k=2 * A, v=3 * A, o=4 * A, lse=5 * A)
+    p.update(kw)
+    return fa.lib().fa_fwd_splitkv_noalloc(p["q"], p["k"], p["v"], p["o"], p["lse"], B, H, T, Tk, d, 1,
+                                           scale, n, None)
+
+
+def test_splitkv_noalloc_checks():
+    # every rejection happens before the scratch buffer is looked up (no HIP call on any of these)
+    for kw in ("q", "k", "v", "o", "lse"):
+        assert call_noalloc(**{kw: None}) == fa.FA_ERR_NULL
+    assert call_noalloc(n=0) == fa.FA_ERR_INVALID_ARG
+    assert call_noalloc(n=4097) == fa.FA_ERR_INVALID_ARG
+    assert call_noalloc(T=-1) == fa.FA_ERR_INVALID_ARG
+    assert call_noalloc(Tk=-1) == fa.FA_ERR_INVALID_ARG
+    assert call_noalloc(Tk=(1 << 22) + 1) == fa.FA_ERR_INVALID_ARG
+    assert call_noalloc(d=96) == fa.FA_ERR_UNSUPPORTED_D
+    assert call_noalloc(scale=0.0) == fa.FA_ERR_INVALID_ARG
+    assert call_noalloc(scale=float("nan")) == fa.FA_ERR_INVALID_ARG
+    assert call_noalloc(q=A + 8) == fa.FA_ERR_ALIGNMENT
+    assert call_noalloc(lse=5 * A + 2) == fa.FA_ERR_ALIGNMENT
+    # an empty problem is a no-op
+    assert call_noalloc(T=0) == fa.FA_OK
+    assert call_noalloc(B=0) == fa.FA_OK
+
+
+def test_splitkv_noalloc_rejects_problems_beyond_its_scratch():
+    lib = fa.lib()
+    # the largest split count whose partial results fit, and one more
+    B, H, T, d = 4, 16, 64, 128
+    per_split = lib.fa_splitkv_workspace_bytes(B, H, T, d, 1)
+    n_fit = NOALLOC_SCRATCH_BYTES // per_split
+    assert lib.fa_splitkv_workspace_bytes(B, H, T, d, n_fit) <= NOALLOC_SCRATCH_BYTES
+    assert lib.fa_splitkv_workspace_bytes(B, H, T, d, n_fit + 1) > NOALLOC_SCRATCH_BYTES
+    assert call_noalloc(B=B, H=H, T=T, Tk=1 << 16, d=d, n=n_fit + 1) == fa.FA_ERR_SCRATCH
+    assert call_noalloc(B=1, H=1, T=1 << 22, Tk=1 << 22, d=128, n=1) == fa.FA_ERR_SCRATCH
+    assert "FA_NOALLOC_SCRATCH_BYTES" in fa.strerror(fa.FA_ERR_SCRATCH)
