@@ -588,7 +588,7 @@ def main(argv=None):
         ms128, ex128 = time_backward(w128, max(5, args.steps // 20), max(2, args.warmup // 20))
         tf128 = BWD_FLOPS_PER_FWD * w128.flops / (ms128 * 1e-3) / 1e12
         backward["d128"] = {"workload": w128.name, "ms_per_step": round(ms128, 5), "tflops": round(tf128, 3),
-                            "median_ms": round(ex128["median_ms"], 5),
+                            "wall_ms": round(ex128["wall_ms"], 5),
                             "roofline": {"bound": "mfma", "achieved": round(tf128, 3), "peak": PEAK_BF16_TFLOPS,
                                          "unit": "TFLOP/s", "frac": round(tf128 / PEAK_BF16_TFLOPS, 4),
                                          "traffic": None}}
