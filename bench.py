@@ -320,6 +320,27 @@ def _event_timer(stream, steps, warmup):
     return timed
 
 
+def _graph_timer(steps, warmup):
+    """A timer for calls too short to outrun their Python launch overhead: `steps` calls captured
+    once into a HIP graph (each call launches on the current stream, the capture stream while
+    capturing), then ms per call from one event pair around a replay of the graph."""
+    import torch
+
+    def timed(fn):
+        fn()  # once eagerly, outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(steps):
+                fn()
+        stream = torch.cuda.current_stream()
+        warm_up(g.replay, max(1, warmup // max(steps, 1)), torch.cuda.synchronize, min_s=0.1)
+        ms = time_region(g.replay, 1, stream, torch.cuda.synchronize)[1] / steps
+        del g
+        return ms
+    return timed
+
+
 # Decode-shaped split-KV workloads: a few new queries per sequence at the end of the 16384-key
 # sequences of the B=4, H=12, d=64 workload (causal, the queries after the keys' prefix).
 DECODE_SHAPES = ((4, 12, 1, 16384, 64), (4, 12, 16, 16384, 64))
@@ -335,7 +356,7 @@ def time_splitkv(steps, warmup):
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
-    timed = _event_timer(stream, steps, warmup)
+    gtimed = _graph_timer(max(steps, 50), warmup)
     decode = []
     for (B, H, T, Tk, d) in DECODE_SHAPES:
         q = to_torch_bf16(make_qkv(B, H, T, d, seed=91)[0], dev)
@@ -345,10 +366,9 @@ def time_splitkv(steps, warmup):
         lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
         n = fa.splitkv_splits(B, H, T, Tk, d)
         ws = torch.empty(fa.splitkv_workspace_bytes(B, H, T, d, n), dtype=torch.uint8, device=dev)
-        ms = timed(lambda: fa.fwd_splitkv(q, k, v, causal=True, n_splits=n, out=o, lse=lse, workspace=ws,
-                                          stream=stream))
-        ms1 = timed(lambda: fa.fwd_splitkv(q, k, v, causal=True, n_splits=1, out=o, lse=lse, workspace=ws,
-                                           stream=stream))
+        # one call is a few tens of microseconds: timed as a graph of `steps` calls (no host gaps)
+        ms = gtimed(lambda: fa.fwd_splitkv(q, k, v, causal=True, n_splits=n, out=o, lse=lse, workspace=ws))
+        ms1 = gtimed(lambda: fa.fwd_splitkv(q, k, v, causal=True, n_splits=1, out=o, lse=lse, workspace=ws))
         # algorithmic HBM bytes: q, k, v read once, o and lse written once (the partial results'
         # round trip through the workspace is the split's own cost, so it is not counted)
         alg = B * H * (2 * T * d * 2 + 2 * Tk * d * 2 + T * 4)
@@ -469,7 +489,10 @@ def cpu_baseline(wl, budget_s=20.0):
     return base, (o_ref, lse_ref), n_heads
 
 
-def cpu_baseline_per_config(budget_heads_s=3.0):
+PER_CONFIG = ("c1", "c2", "c3", "c4", "c5a", "c5b")
+
+
+def cpu_baseline_per_config(names=PER_CONFIG, budget_heads_s=3.0):
     """The oracle timed on every workload: C1-C4 whole (C1 also on one thread); C5a and C5b on whole
     heads of their shape (seeded N(0,1) draws of those heads), as many as fit about `budget_heads_s`
     seconds. The oracle's time does not depend on the values."""
@@ -478,7 +501,7 @@ def cpu_baseline_per_config(budget_heads_s=3.0):
 
     threads = len(os.sched_getaffinity(0))
     out = {}
-    for name in ("c1", "c2", "c3", "c4", "c5a", "c5b"):
+    for name in names:
         wl = WORKLOADS[name]
         for nt in ((threads, 1) if name == "c1" else (threads,)):
             if name in ("c5a", "c5b"):
@@ -652,7 +675,8 @@ def main(argv=None):
         parity = parity_check(wl, o_dev, lse_dev, ref, n_heads)
         print(f"[bench] parity: {parity}", file=sys.stderr, flush=True)
         del ref
-        base["per_config"] = cpu_baseline_per_config()
+        # every workload (the bench's own workload is the object above)
+        base["per_config"] = cpu_baseline_per_config(tuple(n for n in PER_CONFIG if n != args.workload))
         print(f"[bench] cpu baseline per config: {base['per_config']}", file=sys.stderr, flush=True)
 
     profiled = args.workload == PROFILED_WORKLOAD and tiles is None

@@ -24,10 +24,10 @@ def hipcc() -> str:
     return os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
 
 
-def build(extra_flags=(), out: str = LIB) -> str:
+def build(extra_flags=(), out: str = LIB, src: str = SRC) -> str:
     tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"),
-           "-I", os.path.join(PKG, "csrc"), SRC, "-o", tmp]
+           "-I", os.path.join(PKG, "csrc"), src, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"
     msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
@@ -40,5 +40,15 @@ def build(extra_flags=(), out: str = LIB) -> str:
     return out
 
 
+PROBE_SRC = os.path.join(ROOT, "tests", "fp8_mfma_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "libfp8_mfma_probe.so")
+
+
+def build_probe() -> str:
+    """Test infrastructure: the FP8 matrix-instruction accuracy probe the FP8 tests use."""
+    return build(out=PROBE_LIB, src=PROBE_SRC)
+
+
 if __name__ == "__main__":
     print(build())
+    print(build_probe())

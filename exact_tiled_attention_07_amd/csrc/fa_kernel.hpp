@@ -18,7 +18,7 @@
 //     legend; STEP 5 note contrasting per-block masking with separate diagonal handling);
 //   - the softmax of one block runs while the matrix unit computes the next block's scores, the
 //     overlap of non-matrix work with matrix work that the cnblogs page describes for its third
-//     version ("最近在 V3 版本中");
+//     version (the closing section, on V3);
 //   - the per-row logsumexp is written for a backward pass (STEP 4, note on training);
 //   - for short sequences (few Q blocks) two waves may share one block of queries, each walking
 //     every other K/V block, and combine their (m, l, O) at the end with the log-space merge of

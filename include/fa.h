@@ -86,7 +86,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
            int d, int causal, float scale, void* stream);
 
 /*
- * fa_fwd_ex — fa_fwd with the tile shape forced, for the tile-shape study.
+ * fa_fwd_ex — fa_fwd with the tile shape forced, for the tile-shape study. The block size is bounded
+ * by what one program's Q, K, V, score and accumulator blocks can keep on chip, and real kernels pick
+ * it by measuring a few candidates (learn-llm.fim.ai "手写 FlashAttention：拆开 SDPA 这个黑盒",
+ * STEP 3, the note on choosing the block size); the extra arguments name the candidate.
  *   block_m  query rows per workgroup: 32 * waves (one 32-query block per wave), 64 * waves (two per
  *            wave) or 16 * waves (the key split, two waves per block: fa_fwd_ex(..., 64, 64, 4))
  *   block_n  keys per K/V tile staged in LDS

@@ -52,7 +52,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fa_ref.c")
 _SRC_BWD = os.path.join(_HERE, "fa_ref_bwd.c")
 _SRC_SPARSE = os.path.join(_HERE, "fa_ref_sparse.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# FA_ORACLE_LIB names another build of the same sources (the sanitizer test loads an ASan/UBSan one)
+_LIB_PATH = os.environ.get("FA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 

@@ -13,15 +13,15 @@
  *        that materialises the T x T score matrix per head)
  *
  *   the softmax subtracts the row maximum before exponentiating, which leaves the result unchanged
- *       (same page, STEP 2, "为什么要减去最大值": numerator and denominator are both multiplied by
- *        exp(-m), so every exponent is <= 1)
+ *       (same page, STEP 2, the note on why the maximum is subtracted: numerator and denominator
+ *        are both multiplied by exp(-m), so every exponent is <= 1)
  *
  *   causal masking keeps key j for query i only when j <= i: the upper-right part of the T x T grid
  *   is masked (same page, STEP 3, the block-grid legend)
  *
  *   the per-row logsumexp (natural log, over the scaled scores of the visible keys) is returned as
- *   well; it is what the forward pass saves for the backward (same page, STEP 4, "这个 kernel
- *   能拿来训练吗")
+ *   well; it is what the forward pass saves for the backward (same page, STEP 4, the note on whether
+ *   the kernel can be used for training)
  *
  * The softmax is two-pass (max, then exp-sum), not the online recurrence the GPU kernel uses, so the
  * two implementations share neither code nor algorithm. Rows are independent and are spread over
@@ -36,9 +36,7 @@
 #include <string.h>
 #include <omp.h>
 
-#define FA_REF_OK 0
-#define FA_REF_EINVAL (-1)
-#define FA_REF_ENOMEM (-2)
+#include "fa_ref.h"
 
 /* A bf16 value is the top half of an IEEE binary32; widening it to double is exact. */
 static double bf16_bits_to_double(uint16_t bits) {

@@ -35,9 +35,7 @@
 #include <string.h>
 #include <omp.h>
 
-#define FA_REF_OK 0
-#define FA_REF_EINVAL (-1)
-#define FA_REF_ENOMEM (-2)
+#include "fa_ref.h"
 
 static double bwd_bf16_to_double(uint16_t bits) {
   uint32_t u = (uint32_t)bits << 16;

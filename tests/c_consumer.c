@@ -40,7 +40,9 @@ static int host_checks(void) {
    * dereferenced and nothing is launched */
   char* a = (char*)(uintptr_t)0x10000;
   int codes[] = {FA_OK, FA_ERR_NULL, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED_D, FA_ERR_ALIGNMENT,
-                 FA_ERR_HIP, FA_ERR_TILE};
+                 FA_ERR_HIP, FA_ERR_TILE, FA_ERR_SCRATCH};
+  float* lse = (float*)(a + 0x40000);
+  size_t ws;
   size_t i, j;
   fa_plan_info plan;
 
@@ -57,6 +59,37 @@ static int host_checks(void) {
                0.125f, NULL) == FA_ERR_ALIGNMENT, "misaligned q accepted");
   CHECK(fa_fwd(a, a + 0x10000, a + 0x20000, a + 0x30000, (float*)(a + 0x40000), 1, 1, 0, 64, 1,
                0.125f, NULL) == FA_OK, "empty problem rejected");
+  /* the other entry points' checks (each returns before any HIP call) */
+  CHECK(fa_fwd_ex(a, a + 0x10000, a + 0x20000, a + 0x30000, lse, 1, 1, 8, 64, 1, 0.125f, NULL, 96,
+                  64, 3) == FA_ERR_TILE, "unknown tile accepted");
+  CHECK(fa_fwd_ex(a, a + 0x10000, a + 0x20000, a + 0x30000, lse, 1, 1, 8, 64, 1, -1.0f, NULL, 128,
+                  64, 4) == FA_ERR_INVALID_ARG, "negative scale accepted");
+  CHECK(fa_fwd_sparse(a, a + 0x10000, a + 0x20000, a + 0x30000, lse, 2, 3, 8, 64, 1, 0.125f,
+                      (const unsigned char*)(a + 0x50000), 5, NULL) == FA_ERR_INVALID_ARG,
+        "mask_heads 5 accepted for B*H = 6");
+  CHECK(fa_fwd_sparse(a, a + 0x10000, a + 0x20000, a + 0x30000, lse, 1, 1, FA_SPARSE_MAX_T + 1, 64, 1,
+                      0.125f, (const unsigned char*)(a + 0x50000), 1, NULL) == FA_ERR_INVALID_ARG,
+        "sparse T above its limit accepted");
+  CHECK(fa_fwd_partial(a, a + 0x10000, a + 0x20000, (float*)(a + 0x30000), lse, 1, 1, 8, 100, 64, 1,
+                       0.125f, 32, 100, NULL) == FA_ERR_INVALID_ARG, "unaligned k_begin accepted");
+  CHECK(fa_merge((const float*)a, (const float*)(a + 0x10000), 0, a + 0x20000, lse, 1, 1, 8, 64,
+                 NULL) == FA_ERR_INVALID_ARG, "zero parts accepted");
+  ws = fa_splitkv_workspace_bytes(2, 3, 5, 64, 4);
+  CHECK(ws == (size_t)4 * 2 * 3 * 5 * 65 * 4, "workspace bytes %zu", ws);
+  CHECK(fa_splitkv_workspace_bytes(1, 1, 8, 64, 0) == 0, "workspace for zero splits");
+  CHECK(fa_splitkv_splits(4, 12, 1, 16384, 64) >= 1, "split count");
+  CHECK(fa_fwd_splitkv(a, a + 0x10000, a + 0x20000, a + 0x30000, lse, 2, 3, 5, 1000, 64, 1, 0.125f, 4,
+                       a + 0x60000, ws - 1, NULL) == FA_ERR_INVALID_ARG, "small workspace accepted");
+  CHECK(fa_fwd_splitkv_noalloc(a, a + 0x10000, a + 0x20000, a + 0x30000, lse, 1, 1, 1 << 22, 1 << 22,
+                               128, 1, 0.0884f, 1, NULL) == FA_ERR_SCRATCH,
+        "problem beyond the fixed scratch accepted");
+  CHECK(fa_fwd_splitkv_noalloc(a, a + 0x10000, a + 0x20000, a + 0x30000, lse, 1, 1, 0, 100, 64, 1,
+                               0.125f, 1, NULL) == FA_OK, "empty no-allocation problem rejected");
+  CHECK(fa_fwd_fp8(a, a + 0x10000, a + 0x20000, a + 0x30000, lse, 1, 1, 8, 64, 1, 0.125f, 1.0f, 0.0f,
+                   1.0f, NULL) == FA_ERR_INVALID_ARG, "zero descale accepted");
+  CHECK(fa_bwd(a, a + 0x10000, a + 0x20000, a + 0x30000, lse, a + 0x50000, a, a + 0x60000,
+               a + 0x70000, (float*)(a + 0x80000), 1, 1, 8, 64, 1, 0.125f, NULL) == FA_ERR_INVALID_ARG,
+        "dq overlapping q accepted");
   CHECK(fa_fwd_plan(4, 12, 4096, 64, 1, 0, 0, 0, &plan) == FA_OK, "fa_fwd_plan failed");
   CHECK(plan.block_m > 0 && plan.block_n > 0 && plan.waves > 0 && plan.grid > 0,
         "fa_fwd_plan gave an empty launch");

@@ -63,9 +63,42 @@ def test_bench_clock_record_matches_sources():
 
 
 def test_bench_cpu_baseline_small():
-    r = bench.cpu_baseline(WORKLOADS["c1"], budget_s=1.0)
+    r, (o_ref, lse_ref), n_heads = bench.cpu_baseline(WORKLOADS["c1"], budget_s=1.0)
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["cores"] >= 1
     assert r["value"] > 0 and "heads of c1" in r["sample"]
+    assert n_heads == 2 and o_ref.shape == (1, 2, 256, 64) and lse_ref.shape == (1, 2, 256)
+
+
+def test_bench_parity_check_uses_the_oracle_output_and_catches_errors():
+    import torch
+
+    wl = WORKLOADS["c1"]
+    _, ref, n_heads = bench.cpu_baseline(wl, budget_s=1.0)
+    o = torch.from_numpy(ref[0].reshape(wl.B, wl.H, wl.T, wl.d)).to(torch.bfloat16)
+    lse = torch.from_numpy(ref[1].reshape(wl.B, wl.H, wl.T)).float()
+    p = bench.parity_check(wl, o, lse, ref, n_heads)
+    assert p["pass"] and p["n_fail"] == 0 and p["rows"] == wl.B * wl.H * wl.T
+    assert p["max_err_o"] <= 2.0 ** -7  # only the bf16 rounding of the oracle's own output (|O| < 4)
+    o[0, 1, 17, 5] += 0.05  # one element off by more than the tolerance
+    lse[0, 0, 3] += 2e-3
+    p = bench.parity_check(wl, o, lse, ref, n_heads)
+    assert not p["pass"] and p["n_fail"] == 2
+
+
+def test_bench_warm_up_runs_at_least_the_given_steps_and_time():
+    calls = []
+    bench.warm_up(lambda: calls.append(1), 7, lambda: None, min_s=0.05)
+    assert len(calls) >= 7
+
+
+def test_bench_cpu_baseline_per_config_lists_every_workload():
+    assert bench.PER_CONFIG == ("c1", "c2", "c3", "c4", "c5a", "c5b")
+    r = bench.cpu_baseline_per_config(names=("c1", "c5b"), budget_heads_s=0.0)
+    assert set(r) == {"c1", "c1_1thread", "c5b"}
+    assert "1 of 64 heads" in r["c5b"]["sample"]
+    assert r["c1_1thread"]["cores"] == 1
+    for v in r.values():
+        assert v["kind"] == "oracle" and v["value"] > 0
 
 
 def test_bf16_ulp_is_the_spacing_of_bf16():
