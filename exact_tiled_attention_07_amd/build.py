@@ -44,8 +44,14 @@ PROBE_SRC = os.path.join(ROOT, "tests", "fp8_mfma_probe.hip")
 PROBE_LIB = os.path.join(ROOT, "tests", "libfp8_mfma_probe.so")
 
 
+ISSUE_SRC = os.path.join(ROOT, "tests", "issue_rate_probe.hip")
+ISSUE_LIB = os.path.join(ROOT, "tests", "libissue_rate_probe.so")
+
+
 def build_probe() -> str:
-    """Test infrastructure: the FP8 matrix-instruction accuracy probe the FP8 tests use."""
+    """Test infrastructure: the probes the GPU tests run (the FP8 matrix instruction's accuracy, and
+    the issue rates of the forward's inner-loop instructions)."""
+    build(out=ISSUE_LIB, src=ISSUE_SRC)
     return build(out=PROBE_LIB, src=PROBE_SRC)
 
 
