@@ -3,8 +3,10 @@
 Each case plants one mistake in a temporary copy of one oracle C source (a unique text replacement:
 a dropped scale, a mask off by one, a transposed operand, a wrong stride or decode, a missing term of
 the backward, an ignored block mask), builds that copy with gcc, and runs the pin tests of that
-oracle against it in a child process (FA_ORACLE_LIB names the build). Every mutant must fail at
-least one pin; the unmutated sources pass the same pins in the ordinary suite.
+oracle against it in a child process (FA_ORACLE_LIB names the build). The numpy parts of the oracle
+(the log-space merge, the attention of T queries over a key range, the E4M3 decode) are mutated the
+same way in a temporary copy of the source tree, whose own oracle package the child imports. Every
+mutant must fail at least one pin; an unmutated copy passes all of them.
 """
 import os
 import shutil
@@ -119,3 +121,79 @@ def test_every_planted_mistake_fails_a_pin(tmp_path):
     for name, rc, out in results:
         print(f"[mutant] {name}: {'caught' if rc != 0 else 'SURVIVED'}", flush=True)
     assert not survivors, survivors
+
+
+PY_PINS_SPLIT = ["test_oracle_splitkv_pins.py"]
+PY_PINS_FP8 = ["test_oracle_fp8_pins.py"]
+PY_MUTANTS = [
+    ("merge: LSE without the max", [("lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, l)))",
+                                     "lse = np.where(empty, -np.inf, np.log(np.where(empty, 1.0, l)))")],
+     PY_PINS_SPLIT),
+    ("merge: weights not normalised", [("o = (w[..., None] * o_parts).sum(axis=0) / np.where(empty, 1.0, l)[..., None]",
+                                        "o = (w[..., None] * o_parts).sum(axis=0)")], PY_PINS_SPLIT),
+    ("cross: alignment off by one", [("visible = visible & (j <= i + (Tk - T))",
+                                      "visible = visible & (j < i + (Tk - T))")], PY_PINS_SPLIT),
+    ("cross: alignment dropped", [("visible = visible & (j <= i + (Tk - T))", "visible = visible & (j <= i)")],
+     PY_PINS_SPLIT),
+    ("cross: range end inclusive", [("visible = (j >= k_begin) & (j < k_end)", "visible = (j >= k_begin) & (j <= k_end)")],
+     PY_PINS_SPLIT),
+    ("cross: max not subtracted", [("e = np.exp(s - m_safe[:, None])", "e = np.exp(s)")], PY_PINS_SPLIT),
+    ("cross: max left out of the LSE", [("lse[b, h] = np.where(has_key, m_safe + np.log(l_safe), -np.inf)",
+                                         "lse[b, h] = np.where(has_key, np.log(l_safe), -np.inf)")], PY_PINS_SPLIT),
+    ("cross: V in place of K", [("s = float(scale) * (qf @ kf.T)", "s = float(scale) * (qf @ vf.T)")], PY_PINS_SPLIT),
+    ("e4m3: exponent bias 8", [("(1.0 + m / 8.0) * np.exp2(e - 7.0)", "(1.0 + m / 8.0) * np.exp2(e - 8.0)")],
+     PY_PINS_FP8),
+    ("e4m3: subnormal spacing 2^-10", [("np.where(e == 0, m * 2.0 ** -9,", "np.where(e == 0, m * 2.0 ** -10,")],
+     PY_PINS_FP8),
+    ("e4m3: NaN code missed", [("np.where((e == 15) & (m == 7), np.nan, out)", "np.where((e == 15) & (m == 6), np.nan, out)")],
+     PY_PINS_FP8),
+    ("fp8: v descale dropped", [("    v = e4m3_to_f64(v8) * vd\n    return attention_fwd_f64",
+                                 "    v = e4m3_to_f64(v8)\n    return attention_fwd_f64")], PY_PINS_FP8),
+]
+
+
+def copy_tree(dst):
+    """The parts of the source tree the oracle pin tests import, with the built oracle library."""
+    shutil.copytree(ORACLE, os.path.join(dst, "oracle"), ignore=shutil.ignore_patterns("__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "exact_tiled_attention_07_amd"), os.path.join(dst, "exact_tiled_attention_07_amd"),
+                    ignore=shutil.ignore_patterns("__pycache__", "*.so", "csrc"))
+    os.makedirs(os.path.join(dst, "tests"))
+    for f in os.listdir(HERE):
+        if f.endswith(".py") or f == "golden":
+            src = os.path.join(HERE, f)
+            (shutil.copytree if os.path.isdir(src) else shutil.copy)(src, os.path.join(dst, "tests", f))
+    shutil.copy(os.path.join(ROOT, "pytest.ini"), dst)
+    if not os.path.exists(os.path.join(dst, "oracle", "liboracle.so")):
+        subprocess.run([sys.executable, "-c", "import oracle; oracle.build()"], cwd=dst, check=True)
+
+
+def run_pins_in_tree(root, pins):
+    env = {k: v for k, v in os.environ.items() if k != "FA_ORACLE_LIB"}
+    env["OMP_NUM_THREADS"] = "2"
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        *[os.path.join("tests", p) for p in pins]], env=env, cwd=root, capture_output=True,
+                       text=True, timeout=600)
+    return r.returncode, r.stdout[-800:]
+
+
+def test_every_planted_mistake_in_the_numpy_oracle_fails_a_pin(tmp_path):
+    control = str(tmp_path / "control")
+    copy_tree(control)
+    rc, out = run_pins_in_tree(control, PY_PINS_SPLIT + PY_PINS_FP8)
+    assert rc == 0, out
+    trees = []
+    for n, (name, edits, pins) in enumerate(PY_MUTANTS):
+        root = str(tmp_path / f"m{n}")
+        copy_tree(root)
+        path = os.path.join(root, "oracle", "__init__.py")
+        text = open(path).read()
+        for old, new in edits:
+            assert text.count(old) == 1, f"{name}: the planted edit must match exactly once: {old!r}"
+            text = text.replace(old, new)
+        open(path, "w").write(text)
+        trees.append((name, root, pins))
+    with ThreadPoolExecutor(max_workers=4) as ex:
+        results = list(ex.map(lambda a: (a[0], *run_pins_in_tree(a[1], a[2])), trees))
+    for name, rc, out in results:
+        print(f"[mutant] {name}: {'caught' if rc != 0 else 'SURVIVED'}", flush=True)
+    assert not [name for name, rc, _ in results if rc == 0]
