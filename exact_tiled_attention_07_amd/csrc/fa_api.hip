@@ -540,15 +540,24 @@ int launch_bwd_kernels(const void* q, const void* k, const void* v, const void* 
   // dK/dV kernel its Q and dO (as many bytes)
   const int hg = head_group(BH, T, D, causal != 0);
   auto dq_fn = causal ? &fa::fa_bwd_dq_kernel<Cc> : &fa::fa_bwd_dq_kernel<Cf>;
-  auto dkdv_fn = causal ? &fa::fa_bwd_dkdv_kernel<Cc> : &fa::fa_bwd_dkdv_kernel<Cf>;
-  const int rc = launch_kernel(dq_fn, grid, dim3(Cc::THREADS), stream, (const __bf16*)q,
-                               (const __bf16*)k, (const __bf16*)v, (const __bf16*)o, lse,
-                               (const __bf16*)dout, (__bf16*)dq, delta, T, nb, BH, scale, scale_log2,
-                               hg);
+  int rc = launch_kernel(dq_fn, grid, dim3(Cc::THREADS), stream, (const __bf16*)q,
+                         (const __bf16*)k, (const __bf16*)v, (const __bf16*)o, lse,
+                         (const __bf16*)dout, (__bf16*)dq, delta, T, nb, BH, scale, scale_log2, hg);
   if (rc != FA_OK) return rc;
-  return launch_kernel(dkdv_fn, grid, dim3(Cc::THREADS), stream, (const __bf16*)q,
-                       (const __bf16*)k, (const __bf16*)v, lse, (const __bf16*)dout,
-                       (const float*)delta, (__bf16*)dk, (__bf16*)dv, T, nb, BH, scale, scale_log2, hg);
+  auto dkdv = [&](auto fn) {
+    return launch_kernel(fn, grid, dim3(Cc::THREADS), stream, (const __bf16*)q, (const __bf16*)k,
+                         (const __bf16*)v, lse, (const __bf16*)dout, (const float*)delta, (__bf16*)dk,
+                         (__bf16*)dv, T, nb, BH, scale, scale_log2, hg);
+  };
+  if constexpr (D == 64) {  // dK and dV in one pass (196 registers, two waves per SIMD)
+    return dkdv(causal ? &fa::fa_bwd_dkdv_kernel<Cc> : &fa::fa_bwd_dkdv_kernel<Cf>);
+  } else {
+    // d = 128: one pass for dV, then one for dK. Holding both accumulators and both fragment sets
+    // took 319 registers (one wave per SIMD); each single-output pass holds half as much.
+    rc = dkdv(causal ? &fa::fa_bwd_dkdv_kernel<Cc, fa::kDV> : &fa::fa_bwd_dkdv_kernel<Cf, fa::kDV>);
+    if (rc != FA_OK) return rc;
+    return dkdv(causal ? &fa::fa_bwd_dkdv_kernel<Cc, fa::kDK> : &fa::fa_bwd_dkdv_kernel<Cf, fa::kDK>);
+  }
 }
 
 }  // namespace

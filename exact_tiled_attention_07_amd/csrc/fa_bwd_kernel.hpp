@@ -11,7 +11,8 @@
 //   - gradients are accumulated per block (same article, section 2.2); instead of atomic adds into
 //     a global dQ, two kernels each own the rows they write: fa_bwd_dq_kernel owns a block of
 //     queries and walks the K/V tiles (it also writes D), fa_bwd_dkdv_kernel owns a block of keys
-//     and walks the Q/dO tiles. S and dP are computed in both.
+//     and walks the Q/dO tiles. S and dP are computed in both. At d = 128 the second kernel runs as
+//     a dV pass and a dK pass (fewer registers, two waves per SIMD), each recomputing S.
 //
 // gfx950 mapping: the operand layouts, the LDS swizzle, the HBM -> LDS copies and the transposing
 // LDS reads are those of the forward kernel (fa_kernel.hpp):
@@ -275,8 +276,11 @@ __global__ __launch_bounds__(C::THREADS) void fa_bwd_dq_kernel(
 }
 
 // ---- dK, dV: one workgroup per (block of BM keys, batch*head); lane = key. Requires D from
-// fa_bwd_dq_kernel (same stream, launched before).
-template <class C>
+// fa_bwd_dq_kernel (same stream, launched before). PART selects the outputs: kDV, kDK or both. A pass
+// that computes one of them holds one accumulator and the fragments it needs only (dV: K; dK: K
+// and V), so more waves fit on a SIMD; the two passes recompute S = Q K^T each.
+constexpr int kDV = 1, kDK = 2;
+template <class C, int PART = kDV | kDK>
 __global__ __launch_bounds__(C::THREADS) void fa_bwd_dkdv_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const float* __restrict__ lse, const __bf16* __restrict__ dout, const float* __restrict__ delta,
@@ -322,14 +326,15 @@ __global__ __launch_bounds__(C::THREADS) void fa_bwd_dkdv_kernel(
   };
   copy_tile(i0, 0);
 
-  bf16x8 kf[KSTEPS], vf[KSTEPS];
+  constexpr bool DO_DV = (PART & kDV) != 0, DO_DK = (PART & kDK) != 0;
+  bf16x8 kf[KSTEPS], vf[DO_DK ? KSTEPS : 1];
   load_row_frags<KSTEPS>(k + head_off + (int64_t)krow * D, hf, kf);
-  load_row_frags<KSTEPS>(v + head_off + (int64_t)krow * D, hf, vf);
-  f32x16 acc_dk[CB], acc_dv[CB];
+  if constexpr (DO_DK) load_row_frags<KSTEPS>(v + head_off + (int64_t)krow * D, hf, vf);
+  f32x16 acc_dk[DO_DK ? CB : 1], acc_dv[DO_DV ? CB : 1];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    acc_dk[cb] = f32x16{};
-    acc_dv[cb] = f32x16{};
+    if constexpr (DO_DK) acc_dk[cb] = f32x16{};
+    if constexpr (DO_DV) acc_dv[cb] = f32x16{};
   }
 
   vmem_wait<0>();
@@ -350,9 +355,11 @@ __global__ __launch_bounds__(C::THREADS) void fa_bwd_dkdv_kernel(
 #pragma unroll
       for (int st = 0; st < KSTEPS; ++st) {
         const bf16x8 qa = *reinterpret_cast<const bf16x8*>(smem + QR + qb * 32 * RB + fo.row_off[st]);
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(smem + DR + qb * 32 * RB + fo.row_off[st]);
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kf[st], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[st], dp, 0, 0, 0);
+        if constexpr (DO_DK) {
+          const bf16x8 da = *reinterpret_cast<const bf16x8*>(smem + DR + qb * 32 * RB + fo.row_off[st]);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vf[st], dp, 0, 0, 0);
+        }
       }
       // the block's row statistics: registers 4g .. 4g+3 are rows 8g + 4*hf + 0..3
       float lse4[16], d4[16];
@@ -384,8 +391,8 @@ __global__ __launch_bounds__(C::THREADS) void fa_bwd_dkdv_kernel(
         const int r = 2 * p;
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], scale_log2, lse4[r]));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r + 1], scale_log2, lse4[r + 1]));
-        pf[p >> 2][p & 3] = pack_bf16x2(p0, p1);
-        dsf[p >> 2][p & 3] = pack_bf16x2(p0 * (dp[r] - d4[r]), p1 * (dp[r + 1] - d4[r + 1]));
+        if constexpr (DO_DV) pf[p >> 2][p & 3] = pack_bf16x2(p0, p1);
+        if constexpr (DO_DK) dsf[p >> 2][p & 3] = pack_bf16x2(p0 * (dp[r] - d4[r]), p1 * (dp[r + 1] - d4[r + 1]));
       }
       // dV^T += dO^T P and dK^T += Q^T dS over the block's two k-steps
 #pragma unroll
@@ -393,22 +400,26 @@ __global__ __launch_bounds__(C::THREADS) void fa_bwd_dkdv_kernel(
         const int t = 2 * qb + tt;
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-          const s16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(smem + DR + t * 16 * RB + fo.tr_off[cb][0]));
-          const s16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(smem + DR + t * 16 * RB + fo.tr_off[cb][1]));
-          const s16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(smem + QR + t * 16 * RB + fo.tr_off[cb][0]));
-          const s16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_s16x4*)(smem + QR + t * 16 * RB + fo.tr_off[cb][1]));
-          const bf16x8 dot = __builtin_bit_cast(
-              bf16x8, s16x8{dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]});
-          const bf16x8 qtr = __builtin_bit_cast(
-              bf16x8, s16x8{qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]});
-          acc_dv[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, __builtin_bit_cast(bf16x8, pf[tt]),
-                                                               acc_dv[cb], 0, 0, 0);
-          acc_dk[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtr, __builtin_bit_cast(bf16x8, dsf[tt]),
-                                                               acc_dk[cb], 0, 0, 0);
+          if constexpr (DO_DV) {
+            const s16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(smem + DR + t * 16 * RB + fo.tr_off[cb][0]));
+            const s16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(smem + DR + t * 16 * RB + fo.tr_off[cb][1]));
+            const bf16x8 dot = __builtin_bit_cast(
+                bf16x8, s16x8{dlo[0], dlo[1], dlo[2], dlo[3], dhi[0], dhi[1], dhi[2], dhi[3]});
+            acc_dv[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dot, __builtin_bit_cast(bf16x8, pf[tt]),
+                                                                 acc_dv[cb], 0, 0, 0);
+          }
+          if constexpr (DO_DK) {
+            const s16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(smem + QR + t * 16 * RB + fo.tr_off[cb][0]));
+            const s16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_s16x4*)(smem + QR + t * 16 * RB + fo.tr_off[cb][1]));
+            const bf16x8 qtr = __builtin_bit_cast(
+                bf16x8, s16x8{qlo[0], qlo[1], qlo[2], qlo[3], qhi[0], qhi[1], qhi[2], qhi[3]});
+            acc_dk[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qtr, __builtin_bit_cast(bf16x8, dsf[tt]),
+                                                                 acc_dk[cb], 0, 0, 0);
+          }
         }
       }
     }
@@ -417,8 +428,8 @@ __global__ __launch_bounds__(C::THREADS) void fa_bwd_dkdv_kernel(
   }
 
   if (key < T) {
-    store_rows<CB, D>(dk + head_off + (int64_t)key * D, acc_dk, hf, scale);
-    store_rows<CB, D>(dv + head_off + (int64_t)key * D, acc_dv, hf, 1.0f);
+    if constexpr (DO_DK) store_rows<CB, D>(dk + head_off + (int64_t)key * D, acc_dk, hf, scale);
+    if constexpr (DO_DV) store_rows<CB, D>(dv + head_off + (int64_t)key * D, acc_dv, hf, 1.0f);
   }
 }
 

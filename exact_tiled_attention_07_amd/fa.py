@@ -1,7 +1,7 @@
 """ctypes binding of libfa.so (include/fa.h): argument marshalling only.
 
 Every step of the attention forward runs in the gfx950 HIP kernel behind ``fa_fwd``, and every step
-of the backward in the two kernels behind ``fa_bwd``; this module checks tensor metadata, allocates
+of the backward in the kernels behind ``fa_bwd``; this module checks tensor metadata, allocates
 outputs with torch when the caller gives none, and passes raw device pointers plus the current HIP
 stream. There is no fallback: if ``libfa.so`` is missing or a call fails, it raises.
 """

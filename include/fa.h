@@ -277,8 +277,9 @@ int fa_fwd_fp8(const void* q, const void* k, const void* v, void* o, float* lse,
  *   B, H, T, causal, scale, stream: as for fa_fwd (o and lse must come from fa_fwd with the same
  *   q, k, causal and scale)
  *   d        head dimension: 64 or 128
- * The outputs dq, dk, dv and delta must not overlap each other or any input. Two kernels run in
- * order on `stream` (dQ and D, then dK and dV); no atomics, no allocation.
+ * The outputs dq, dk, dv and delta must not overlap each other or any input. The kernels run in
+ * order on `stream`: dQ and D, then dK and dV (at d = 128 one pass for dV and one for dK); no
+ * atomics, no allocation.
  * Returns FA_OK or a negative fa_status (checked before anything is launched).
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
