@@ -590,8 +590,8 @@ int fa_splitkv_splits(int B, int H, int T, int Tk, int d) {
     return 1;
   // as many workgroups as two per compute unit hold at once (not more: a second round would wait
   // for the first), with at least 8 key tiles (512 keys) per range and at most 256 ranges: the
-  // merge reads a row's parts a few at a time, so for few rows many parts cost more latency than
-  // the finer split saves (one head, 2^20 keys: 90 us with 256 ranges, 99 us with 512)
+  // merge loads a row's parts 16 at a time, so for few rows many parts cost more latency than the
+  // finer split saves (one head, 2^20 keys: 85 us with 256 ranges, 92 us with 512, 121 with 128)
   const int64_t base = (int64_t)((T + 127) / 128) * B * H;
   const int64_t want = 512 / base;
   const int64_t most = std::max(1, ((Tk + FA_PARTIAL_KEY_ALIGN - 1) / FA_PARTIAL_KEY_ALIGN) / 8);

@@ -13,8 +13,12 @@
 namespace fa {
 
 // One thread per 4 channels of a row: D/4 threads per row, 256 / (D/4) rows per workgroup. The
-// kernel is bound by HBM traffic (every part's O row is read once); the loads of several parts are
-// issued together so that their latencies overlap.
+// kernel is bound by HBM traffic (every part's O row is read once) or, for few rows, by the latency
+// of its loads: each chunk of up to U parts is loaded with all its loads in flight together, and the
+// chunks are combined with a running maximum (what earlier chunks accumulated is rescaled by
+// exp(m_old - m_new) when a later chunk raises it). With at most U parts there is a single chunk
+// and the result is that of the two-pass form: the weights exp(LSE_s - max_s LSE_s) summed in part
+// order.
 template <int D>
 __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__ o_parts,
                                                        const float* __restrict__ lse_parts,
@@ -22,7 +26,7 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
                                                        float* __restrict__ lse, int64_t rows) {
   constexpr int TPR = D / 4;
   constexpr int RPB = 256 / TPR;
-  constexpr int U = 4;  // parts per batch of loads
+  constexpr int U = 16;  // parts per chunk of loads
   // a long grid is folded into x and z (32-bit work-item counts per dimension)
   const int64_t row = ((int64_t)blockIdx.z * gridDim.x + blockIdx.x) * RPB + threadIdx.x / TPR;
   const int c4 = threadIdx.x % TPR;
@@ -30,42 +34,41 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(const float* __restrict__
   const float* lp = lse_parts + row;
   const float* op = o_parts + row * D + 4 * c4;
   const int64_t lstride = rows, ostride = rows * D;
-  // pass 1: the largest part LSE of the row
-  float m = -__builtin_inff();
-  int s = 0;
-  for (; s + 2 * U <= n_parts; s += 2 * U) {
-    float x[2 * U];
-#pragma unroll
-    for (int e = 0; e < 2 * U; ++e) x[e] = lp[(s + e) * lstride];
-#pragma unroll
-    for (int e = 0; e < 2 * U; ++e) m = fmaxf(m, x[e]);
-  }
-  for (; s < n_parts; ++s) m = fmaxf(m, lp[s * lstride]);
-  // pass 2: weights exp(LSE_s - m), their sum and the weighted sum of the parts' O
+  float m = -__builtin_inff();  // largest part LSE so far
+  float l = 0.0f;               // sum of exp(LSE_s - m) so far
   float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  float l = 0.0f;
-  if (m > -__builtin_inff()) {
-    auto add = [&](float lse_s, float4 x) {
-      const float wgt = expf(lse_s - m);  // 0 for an empty part (LSE_s = -inf)
-      l += wgt;
-      acc[0] += wgt * x.x;
-      acc[1] += wgt * x.y;
-      acc[2] += wgt * x.z;
-      acc[3] += wgt * x.w;
-    };
-    s = 0;
-    for (; s + U <= n_parts; s += U) {
-      float ls[U];
-      float4 xs[U];
+  for (int s = 0; s < n_parts; s += U) {
+    float ls[U];
+    float4 xs[U];
 #pragma unroll
-      for (int e = 0; e < U; ++e) {
+    for (int e = 0; e < U; ++e) {
+      if (s + e < n_parts) {  // n_parts is the same for every lane: a uniform branch
         ls[e] = lp[(s + e) * lstride];
         xs[e] = *reinterpret_cast<const float4*>(op + (s + e) * ostride);
+      } else {
+        ls[e] = -__builtin_inff();
+        xs[e] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
       }
-#pragma unroll
-      for (int e = 0; e < U; ++e) add(ls[e], xs[e]);
     }
-    for (; s < n_parts; ++s) add(lp[s * lstride], *reinterpret_cast<const float4*>(op + s * ostride));
+    float mc = m;
+#pragma unroll
+    for (int e = 0; e < U; ++e) mc = fmaxf(mc, ls[e]);
+    if (mc > -__builtin_inff()) {
+      const float r = expf(m - mc);  // 0 while nothing was seen (m = -inf), 1 if m is unchanged
+      l *= r;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[c] *= r;
+#pragma unroll
+      for (int e = 0; e < U; ++e) {
+        const float wgt = expf(ls[e] - mc);  // 0 for an empty part (LSE_s = -inf)
+        l += wgt;
+        acc[0] += wgt * xs[e].x;
+        acc[1] += wgt * xs[e].y;
+        acc[2] += wgt * xs[e].z;
+        acc[3] += wgt * xs[e].w;
+      }
+      m = mc;
+    }
   }
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
