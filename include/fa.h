@@ -78,8 +78,9 @@ typedef enum fa_status {
  *     partial results in log space; ijyty.com FlashAttention article, section 2.1) when causal,
  *     nq >= 8, grid <= 384 and (nq >= 16 or grid <= 288), or non-causal and grid <= 256;
  *   - else 128-key tiles when nq >= 5 and (nq <= 8 or grid <= 768).
- * At d = 128, non-causal launches with T >= 2048 take 256 queries (8 waves) per workgroup. Both give the exact result up to rounding order; a fixed problem always takes the same
- * launch, so repeated calls are bit-identical.
+ * At d = 128, non-causal launches with T >= 2048 take 256 queries (8 waves) per workgroup. Every
+ * launch gives the exact result up to rounding order; a fixed problem always takes the same launch,
+ * so repeated calls are bit-identical.
  * Returns FA_OK or a negative fa_status.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int T,
