@@ -86,6 +86,44 @@ def test_merge_against_oracle(n, T, d):
     np.testing.assert_allclose(lse[live], lse_ref[live], rtol=0, atol=MERGE_LSE_TOL)
 
 
+@pytest.mark.parametrize("n", [16, 17, 33, 48])
+def test_merge_chunk_boundaries(n):
+    # the merge takes the parts 16 at a time with a running maximum; rows built so that the first
+    # chunk is all empty, the maximum sits in the last chunk (every later chunk rescales what came
+    # before), the maximum sits in the first chunk, only the last part is non-empty, or none is
+    B, H, T, d = 1, 2, 40, 64
+    op, lp = make_partials(n, B, H, T, d, seed=77 + n, p_empty=0.0)
+    ramp = np.linspace(-20.0, 20.0, n, dtype=np.float32)
+    e = min(16, n - 1)                                 # first chunk empty (n > 16), the rest random
+    lp[:e, 0, 0, 0:8] = -np.inf
+    op[:e, 0, 0, 0:8] = 0.0
+    lp[:, 0, 0, 8:16] = ramp[:, None]                  # maximum in the last part
+    lp[:, 0, 0, 16:24] = ramp[::-1, None]              # maximum in the first part
+    lp[:-1, 0, 1, 0:8] = -np.inf                       # only the last part has keys
+    op[:-1, 0, 1, 0:8] = 0.0
+    lp[:, 0, 1, 8:12] = -np.inf                        # no part has keys
+    op[:, 0, 1, 8:12] = 0.0
+    say(f"[gpu splitkv] merge chunk boundaries n={n}")
+    o, lse = fa.merge(torch.from_numpy(op).to(DEV), torch.from_numpy(lp).to(DEV))
+    torch.cuda.synchronize()
+    o, lse = np64(o), np64(lse)
+    o_ref, lse_ref = oracle.merge_partials(op, lp)
+    empty = np.isneginf(lse_ref)
+    assert empty[0, 1, 8:12].all() and empty.sum() == 4
+    np.testing.assert_array_equal(np.isneginf(lse), empty)
+    assert np.all(o[empty] == 0.0)
+    live = ~empty
+    bound = np.maximum(np.abs(o_ref[live]), 2.0 ** -126) * (2.0 ** -8) + MERGE_O_TOL * (1 + np.abs(o_ref[live]))
+    err = np.abs(o[live] - o_ref[live])
+    say(f"[gpu splitkv] merge chunk boundaries n={n} max err O {err.max():.3e}")
+    assert np.all(err <= bound)
+    np.testing.assert_allclose(lse[live], lse_ref[live], rtol=0, atol=MERGE_LSE_TOL)
+    # a row with a single non-empty part is that part, rounded once
+    one = o[0, 1, 0:8]
+    assert np.array_equal(one, np64(torch.from_numpy(op[-1, 0, 1, 0:8]).to(torch.bfloat16)))
+    np.testing.assert_array_equal(lse[0, 1, 0:8], lp[-1, 0, 1, 0:8].astype(np.float64))
+
+
 def test_merge_of_one_part_is_rounding():
     op, lp = make_partials(1, 1, 4, 300, 64, seed=9, p_empty=0.0)
     opt, lpt = torch.from_numpy(op).to(DEV), torch.from_numpy(lp).to(DEV)
