@@ -553,7 +553,6 @@ int launch_bwd_kernels(const void* q, const void* k, const void* v, const void* 
     // dK and dV in one pass (196 registers, two waves per SIMD). The two passes of d = 128 would
     // fit in 112 and 164 registers here, but their second computation of S and second reads of Q
     // and dO cost more than the extra waves return: 16% slower at causal B4 H12 T4096.
-
     return dkdv(causal ? &fa::fa_bwd_dkdv_kernel<Cc> : &fa::fa_bwd_dkdv_kernel<Cf>);
   } else {
     // d = 128: one pass for dV, then one for dK. Holding both accumulators and both fragment sets
