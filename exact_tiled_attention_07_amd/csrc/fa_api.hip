@@ -62,24 +62,34 @@ int fold_grid(int64_t n, int threads, int splits, dim3* grid) {
 using KernelFn = void (*)(const __bf16*, const __bf16*, const __bf16*, __bf16*, float*, int, int, int,
                           float, const uint8_t*, int, int, int, int, int, int);
 
-// Heads per group within an XCD (see map_block). Causal: all of the XCD's heads interleaved, so
-// that the Q blocks with the most tiles of every head start first and the short ones fill the end
-// (grouping heads there left XCDs idle at the end of each group: 660-750 against 796 TFLOP/s at
-// B4 H12 T4096 d64). Non-causal, where every workgroup has the same work: the largest divisor of
-// B*H/8 whose K and V fit in half of an XCD's 4 MB L2, so that a group's Q blocks share its K/V
-// tiles in L2 (B4 H16 T8192 d128: 1105-1108 against 1076-1103 TFLOP/s on two boxes; non-causal
-// d64 shapes 0.2-0.4% faster). The backward kernels take the same groups (its B4 H16 T8192 d128:
-// 680-682 against 663-665 TFLOP/s on one box), and so does the FP8 forward with its one-byte K and V
-// (elem_bytes = 1; B4 H16 T8192 d128: 1801-1811 against 1784-1785). Used only when B*H is a
-// multiple of 8.
+// Heads per group within an XCD (see map_block): the largest divisor of B*H/8 whose K and V fit in
+// a byte budget, so that the XCD's workgroups stream the K/V of that many heads at a time. Used only
+// when B*H is a multiple of 8.
+// - Non-causal, where every workgroup has the same work: half of the XCD's 4 MB L2, so that a
+//   group's Q blocks share its K/V tiles in L2 (B4 H16 T8192 d128: 1105-1108 against 1076-1103
+//   TFLOP/s on two boxes; non-causal d64 shapes 0.2-0.4% faster).
+// - Causal: 16 MB. The heads of a group are interleaved so that the Q blocks with the most tiles
+//   start first and the short ones fill the end, and grouping fewer heads than the budget allows
+//   leaves XCDs idle at the end of each group (B4 H12 T4096 d64, 1 MB of K/V per head: 652-737
+//   against 796 TFLOP/s). Beyond the budget (the K/V that eight XCDs stream at once no longer fit
+//   in half of the 256 MB last-level cache, a reading consistent with these measurements) larger
+//   groups lose time: with all heads interleaved, B4 H16 T32768 d64 (8 MB per head) ran
+//   at 881-917 TFLOP/s against 941-948 in groups of 2 or 4, B4 H16 T16384 d128 at 984-995 against
+//   1065-1081, B1 H32 T65536 d64 (16 MB) at 933-959 against 953-965 in groups of 1 or 2; at
+//   B4 H12 T16384 d64 (4 MB) groups of 3 and all 6 heads are level (909-920), and at T8192 d64
+//   (2 MB) all 6 heads are fastest (875-878 against 871-876 for 3, 834-840 for 2).
+// The backward kernels take the same groups, and so does the FP8 forward with its one-byte K and V
+// (elem_bytes = 1; non-causal B4 H16 T8192 d128: 1801-1811 against 1784-1785), and the block-sparse
+// forward (causal, 25% of the blocks: B4 H12 T16384 d64 0.517-0.518 against 0.531 ms with all heads
+// interleaved, B4 H16 T32768 d64 2.59-2.61 against 2.91 ms).
 constexpr int64_t kHeadGroupBytes = int64_t{2} << 20;
+constexpr int64_t kCausalHeadGroupBytes = int64_t{16} << 20;
 
 int head_group(int64_t BH, int64_t Tk, int d, bool causal, int elem_bytes = 2) {
   if (BH % 8 != 0) return 1;
   const int per = (int)(BH / 8);
-  if (causal) return per;
   const int64_t kv = std::max<int64_t>(Tk * d * elem_bytes * 2, 1);
-  const int64_t gmax = std::max<int64_t>(1, kHeadGroupBytes / kv);
+  const int64_t gmax = std::max<int64_t>(1, (causal ? kCausalHeadGroupBytes : kHeadGroupBytes) / kv);
   int g = per;
   while (g > 1 && (g > gmax || per % g != 0)) --g;
   return g;
@@ -257,7 +267,7 @@ int launch_sparse(const void* q, const void* k, const void* v, void* o, float* l
   return launch_kernel(fn, grid, dim3(256), stream, (const __bf16*)q,
                        (const __bf16*)k, (const __bf16*)v, (__bf16*)o, lse, T, nq, BH,
                        scale * fa::kLog2e, (const uint8_t*)block_mask, mask_heads, 0, 0, 0, 0,
-                       BH / 8);
+                       head_group(BH, T, d, causal != 0));
 }
 
 // Partial forward over a key range: the default tile with the range selection and fp32 output.
@@ -659,6 +669,7 @@ int fa_fwd_plan(int B, int H, int T, int d, int causal, int block_m, int block_n
   p.grid = (long long)p.q_blocks * B * H;
   p.lds_bytes = tile->lds_bytes;
   p.key_split = tile->key_split;
+  p.head_group = head_group((int64_t)B * H, T, d, causal != 0);
   // K/V tiles per Q block: up to the diagonal when causal, all of them otherwise.
   long long tiles_per_head = 0;
   for (int qb = 0; qb < p.q_blocks; ++qb) {

@@ -37,7 +37,8 @@ class FaError(RuntimeError):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int), ("block_n", ctypes.c_int), ("waves", ctypes.c_int),
                 ("q_blocks", ctypes.c_int), ("grid", ctypes.c_longlong),
-                ("lds_bytes", ctypes.c_int), ("kv_tiles", ctypes.c_longlong), ("key_split", ctypes.c_int)]
+                ("lds_bytes", ctypes.c_int), ("kv_tiles", ctypes.c_longlong), ("key_split", ctypes.c_int),
+                ("head_group", ctypes.c_int)]
 
 
 class _Int(ctypes.c_int):

@@ -115,6 +115,9 @@ typedef struct fa_plan_info {
   int key_split;   /* 1, or 2: two waves share each 32-query block, each taking every other K/V tile,
                       and merge their partial results in log space (a default at d = 64 for
                       the short sequences described at fa_fwd) */
+  int head_group;  /* when B*H is a multiple of 8 each of the 8 XCDs takes B*H/8 heads, and streams
+                      their K/V head_group heads at a time: the largest divisor of B*H/8 whose K and
+                      V fit in 16 MB (causal) or 2 MB (non-causal); 1 otherwise */
 } fa_plan_info;
 
 /*

@@ -163,6 +163,34 @@ def test_plan_default_tile_for_short_sequences():
     assert fa.plan(1, 1, 8, 64, True, 128, 64, 4)["key_split"] == 1
 
 
+def test_plan_head_groups():
+    # heads per XCD group: the largest divisor of B*H/8 whose K and V (T * d * 2 bytes each) fit in
+    # 16 MB when causal, 2 MB otherwise; 1 when B*H is not a multiple of 8
+    def hg(B, H, T, d, causal):
+        return fa.plan(B, H, T, d, causal)["head_group"]
+    MiB = 1 << 20
+
+    def expect(B, H, T, d, causal):
+        if (B * H) % 8:
+            return 1
+        per, kv = B * H // 8, T * d * 2 * 2
+        gmax = max(1, (16 * MiB if causal else 2 * MiB) // kv)
+        return max(g for g in range(1, per + 1) if per % g == 0 and (g <= gmax or g == 1))
+    cases = [(4, 12, 4096, 64, True, 6),      # 1 MB per head: all 6 of the XCD's heads
+             (4, 12, 8192, 64, True, 6),      # 2 MB
+             (4, 12, 16384, 64, True, 3),     # 4 MB: at most 4 heads, a divisor of 6
+             (4, 16, 32768, 64, True, 2),     # 8 MB
+             (1, 32, 65536, 64, True, 1),     # 16 MB
+             (4, 16, 8192, 128, True, 4),     # 4 MB at d = 128
+             (4, 16, 16384, 128, True, 2),
+             (4, 16, 8192, 128, False, 1),    # non-causal: 2 MB budget, 4 MB per head
+             (4, 16, 2048, 64, False, 4),     # non-causal: 512 KB per head, 4 fit, a divisor of 8
+             (3, 12, 4096, 64, True, 1),      # B*H = 36: not a multiple of 8
+             (1, 8, 1000, 64, True, 1)]       # one head per XCD
+    for B, H, T, d, causal, want in cases:
+        assert hg(B, H, T, d, causal) == want == expect(B, H, T, d, causal), (B, H, T, d, causal)
+
+
 def test_plan_errors():
     with pytest.raises(fa.FaError) as e:
         fa.plan(1, 1, 8, 80)

@@ -138,6 +138,33 @@ def test_one_head_very_long_sequence():
     assert_parity(stats, f"T={T}")
 
 
+@pytest.mark.parametrize("B,H,T,d,hg", [(4, 16, 16384, 64, 4), (2, 16, 32768, 64, 2), (4, 16, 8192, 128, 4)])
+def test_causal_head_groups(B, H, T, d, hg):
+    # causal launches whose XCDs take their heads in groups smaller than all of them (K and V of a
+    # group within 16 MB): every row is written (outputs start as NaN), and whole heads of the first
+    # group, of the next group and of the last one match the oracle on every row
+    assert fa.plan(B, H, T, d, True)["head_group"] == hg
+    BH = B * H
+    qb, kb, vb = make_qkv(B, H, T, d, seed=B * H + T + d)
+    scale = 1.0 / math.sqrt(d)
+    say(f"[gpu] causal head groups of {hg}: B{B} H{H} T{T} d{d}")
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, T), float("nan"), dtype=torch.float32, device=DEV)
+    fa.fwd(q, k, v, causal=True, scale=scale, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any().item() and not torch.isnan(lse).any().item()
+    # head b*H + h runs on XCD (b*H + h) % 8 in group (b*H + h) // (8 * hg) of that XCD
+    for bh in sorted({0, 8 * hg - 1, 8 * hg, BH - 1}):
+        sel = [x.reshape(1, BH, T, d)[:, bh:bh + 1] for x in (qb, kb, vb)]
+        o_ref, lse_ref = oracle.attention_fwd(*sel, True, scale)
+        o_g = o.view(BH, T, d)[bh:bh + 1].float().cpu().numpy().reshape(1, 1, T, d)
+        lse_g = lse.view(BH, T)[bh:bh + 1].cpu().numpy().reshape(1, 1, T)
+        stats = compare(o_g, lse_g, o_ref, lse_ref)
+        say(f"[gpu] head groups of {hg}, head {bh}: {stats}")
+        assert_parity(stats, f"B{B} H{H} T{T} d{d} head {bh}")
+
+
 FA_MAX_T = 1 << 22  # include/fa.h: the largest accepted sequence length
 
 
