@@ -695,7 +695,7 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16 inputs)",
+        "data": "synthetic (seeded normal draws times config.input_sigma, rounded to bf16)",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "T": wl.T, "d": wl.d,
                    "causal": wl.causal, "input_sigma": wl.sigma, "scale": wl.scale,
                    "tiles": args.tiles or "default"},
