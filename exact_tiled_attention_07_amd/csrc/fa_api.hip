@@ -86,7 +86,7 @@ constexpr int64_t kHeadGroupBytes = int64_t{2} << 20;
 constexpr int64_t kCausalHeadGroupBytes = int64_t{16} << 20;
 
 int head_group(int64_t BH, int64_t Tk, int d, bool causal, int elem_bytes = 2) {
-  if (BH % 8 != 0) return 1;
+  if (BH <= 0 || BH % 8 != 0) return 1;  // (an empty problem launches nothing)
   const int per = (int)(BH / 8);
   const int64_t kv = std::max<int64_t>(Tk * d * elem_bytes * 2, 1);
   const int64_t gmax = std::max<int64_t>(1, (causal ? kCausalHeadGroupBytes : kHeadGroupBytes) / kv);

@@ -171,7 +171,7 @@ def test_plan_head_groups():
     MiB = 1 << 20
 
     def expect(B, H, T, d, causal):
-        if (B * H) % 8:
+        if B * H == 0 or (B * H) % 8:
             return 1
         per, kv = B * H // 8, T * d * 2 * 2
         gmax = max(1, (16 * MiB if causal else 2 * MiB) // kv)
@@ -186,7 +186,8 @@ def test_plan_head_groups():
              (4, 16, 8192, 128, False, 1),    # non-causal: 2 MB budget, 4 MB per head
              (4, 16, 2048, 64, False, 4),     # non-causal: 512 KB per head, 4 fit, a divisor of 8
              (3, 12, 4096, 64, True, 1),      # B*H = 36: not a multiple of 8
-             (1, 8, 1000, 64, True, 1)]       # one head per XCD
+             (1, 8, 1000, 64, True, 1),       # one head per XCD
+             (0, 8, 1000, 64, True, 1)]       # no heads: nothing is launched, the plan says 1
     for B, H, T, d, causal, want in cases:
         assert hg(B, H, T, d, causal) == want == expect(B, H, T, d, causal), (B, H, T, d, causal)
 
