@@ -96,6 +96,34 @@ def test_sparse_long_sequence():
     check(qb, kb, vb, mask, True, 0.125, "T=16384")
 
 
+def test_sparse_head_groups():
+    # B4 H16 T16384 causal: each XCD's 8 heads run 4 at a time (the K/V budget of causal launches);
+    # one mask for every head, 25% of the blocks plus the diagonal ones. Every row is written (the
+    # outputs start as NaN), and whole heads on both sides of each group boundary match the oracle
+    B, H, T, d = 4, 16, 16384, 64
+    assert fa.plan(B, H, T, d, True)["head_group"] == 4
+    BH = B * H
+    qb, kb, vb = make_qkv(B, H, T, d, seed=37)
+    mask = random_mask(T, 1, 0.25, 11)
+    for i in range(mask.shape[1]):
+        mask[0, i, 2 * i:2 * i + 2] = 1
+    say(f"[gpu sparse] head groups B{B} H{H} T{T}")
+    q, k, v = (to_torch_bf16(x, DEV) for x in (qb, kb, vb))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, T), float("nan"), dtype=torch.float32, device=DEV)
+    fa.fwd_sparse(q, k, v, torch.from_numpy(mask).to(DEV), causal=True, scale=0.125, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any().item() and not torch.isnan(lse).any().item()
+    for bh in (0, 31, 32, 63):  # heads 0..31 form the first group of every XCD, 32..63 the second
+        sel = [x.reshape(1, BH, T, d)[:, bh:bh + 1] for x in (qb, kb, vb)]
+        o_ref, lse_ref = oracle.attention_fwd_blockmask(*sel, True, 0.125, mask, 128, 64)
+        o_g = o.view(BH, T, d)[bh:bh + 1].float().cpu().numpy().astype(np.float64).reshape(1, 1, T, d)
+        lse_g = lse.view(BH, T)[bh:bh + 1].cpu().numpy().astype(np.float64).reshape(1, 1, T)
+        stats = compare(o_g, lse_g, o_ref, lse_ref)
+        say(f"[gpu sparse] head groups, head {bh}: {stats}")
+        assert_parity(stats, f"sparse head groups, head {bh}")
+
+
 def test_sparse_longest_sequence_full_tile_list():
     # FA_SPARSE_MAX_T = 65536, non-causal: 5% of the blocks plus the diagonal ones, and the first and
     # last query blocks with every key block set, so their tile lists hold the 1024 tiles a list
