@@ -138,6 +138,41 @@ def test_bwd_long_heads_sampled_rows(B, H, T, d, causal):
         say(f"[gpu bwd] long heads {name}: {st['max_ratio']:.4f}/{st['rms_ratio']:.4f}")
 
 
+@pytest.mark.parametrize("B,H,T,d", [(4, 16, 8192, 128), (4, 16, 16384, 64)])
+def test_bwd_causal_head_groups(B, H, T, d):
+    # causal launches whose XCDs take their 8 heads 4 at a time (the K/V budget of causal launches,
+    # used by both backward kernels): every gradient row is written (outputs start as NaN) and rows
+    # sampled in the heads on both sides of each group boundary (heads 0..31 form every XCD's first
+    # group, 32..63 its second) match the row oracle
+    assert fa.plan(B, H, T, d, True)["head_group"] == 4
+    qb, kb, vb, dob = inputs(B, H, T, 120 + d, d=d)
+    scale = 1.0 / math.sqrt(d)
+    say(f"[gpu bwd] causal head groups B={B} H={H} T={T} d={d}")
+    q, k, v, do = (to_torch_bf16(x, DEV) for x in (qb, kb, vb, dob))
+    o, lse = fa.fwd(q, k, v, causal=True, scale=scale)
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    delta = torch.full_like(lse, float("nan"))
+    fa.bwd(q, k, v, o, lse, do, causal=True, scale=scale, dq=dq, dk=dk, dv=dv, delta=delta)
+    torch.cuda.synchronize()
+    for t in (dq, dk, dv, delta):
+        assert not torch.isnan(t).any().item()
+    rng = np.random.default_rng(T + d + 1)
+    rows = sorted({bh * T + i for bh in (0, 31, 32, 63)
+                   for i in [0, 1, 127, 128, T // 2, T - 1] + rng.integers(0, T, 10).tolist()})
+    idx = torch.as_tensor(rows, dtype=torch.int64, device=DEV)
+    got = [t.reshape(-1, d).index_select(0, idx).float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv)]
+    got.append(delta.reshape(-1).index_select(0, idx).cpu().numpy().astype(np.float64))
+    ref = oracle.attention_bwd_rows(qb, kb, vb, dob, True, scale, rows, rows)
+    qa, ka, va, da = (np.abs(bf16_bits_to_f32(x).astype(np.float64)) for x in (qb, kb, vb, dob))
+    cancel = d * 2.0 ** -24 * float(da.sum(axis=-1).max()) * float(va.max())
+    floors = (2 * scale * float(ka.max()) * cancel, 2 * scale * float(qa.max()) * cancel, 0.0, 0.0)
+    n = len(rows)
+    for name, g, r, a in zip(("dq", "dk", "dv", "delta"), got, ref, floors):
+        shape = (1, 1, n, d) if name != "delta" else (1, 1, n)
+        st = grad_tolerance(name, g.reshape(shape), r.reshape(shape), a)
+        say(f"[gpu bwd] head groups {name}: {st['max_ratio']:.4f}/{st['rms_ratio']:.4f}")
+
+
 @pytest.mark.parametrize("causal", [True, False])
 def test_bwd_other_scales_and_wide_scores(causal):
     check(*inputs(2, 2, 300, 77), causal, 0.01, "scale=0.01")
