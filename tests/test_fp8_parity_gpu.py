@@ -149,6 +149,33 @@ def test_fp8_long_head_sampled_rows():
     check(q8, k8, v8, scales, True, 0.125, "T=2^18 fp8 sampled", rows=rows)
 
 
+def test_fp8_causal_head_groups():
+    # B4 H16 T32768 d64, causal: with one-byte K and V a head holds 4 MB of K/V, so each XCD takes its
+    # 8 heads 4 at a time (the K/V budget of causal launches). Every row is written (the outputs start
+    # as NaN) and rows sampled in the heads on both sides of the group boundary (heads 0..31 form
+    # every XCD's first group, 32..63 its second) satisfy the error bounds against the oracle
+    B, H, T, d = 4, 16, 32768, 64
+    q8, k8, v8, scales = make_qkv_fp8(B, H, T, d, seed=19)
+    say(f"[gpu fp8] causal head groups B{B} H{H} T{T} d{d}")
+    t = [torch.from_numpy(x).to(DEV) for x in (q8, k8, v8)]
+    o = torch.full((B, H, T, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((B, H, T), float("nan"), dtype=torch.float32, device=DEV)
+    fa.fwd_fp8(*t, *scales, causal=True, scale=0.125, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert not torch.isnan(o).any().item() and not torch.isnan(lse).any().item()
+    rng = np.random.default_rng(19)
+    rows = sorted({(bh // H, bh % H, int(i)) for bh in (0, 31, 32, 63)
+                   for i in [0, 1, 63, 64, T // 2, T - 1] + rng.integers(0, T, 6).tolist()})
+    got_o = np.stack([o[b, h, i].float().cpu().numpy().astype(np.float64) for b, h, i in rows])
+    got_l = np.array([float(lse[b, h, i]) for b, h, i in rows])
+    bound, lbound, pred = error_model(q8, k8, v8, scales, True, 0.125, rows)
+    o_ref, lse_ref = oracle.attention_fwd_fp8_rows(q8, k8, v8, True, 0.125, *scales, rows)
+    err, lerr = np.abs(got_o - o_ref), np.abs(got_l - lse_ref)
+    say(f"[gpu fp8] head groups max ratio to bound {(err / bound).max():.3f} lse ratio {(lerr / lbound).max():.3f}")
+    assert np.all(err <= bound) and np.all(lerr <= lbound)
+    assert float((err ** 2).mean()) <= MSE_FACTOR * float(pred.mean())
+
+
 def test_fp8_scales_and_descales():
     q8, k8, v8, scales = make_qkv_fp8(2, 2, 300, 64, seed=81)
     check(q8, k8, v8, scales, True, 0.01, "scale 0.01")
