@@ -483,13 +483,31 @@ def cpu_baseline(wl, budget_s=20.0):
     dt = time.perf_counter() - t0
     fl = _oracle_flops(wl, T, T, n_heads)
     base = {"value": float(fl / dt / 1e12), "unit": "TFLOP/s", "cores": oracle.threads_used(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{n_heads} of {n_heads_total} heads of {wl.name} (all {T} rows each), "
                       f"fp64 two-pass oracle, {dt:.1f} s"}
     return base, (o_ref, lse_ref), n_heads
 
 
 PER_CONFIG = ("c1", "c2", "c3", "c4", "c5a", "c5b")
+
+
+def compulsory_bytes(wl):
+    """HBM bytes a launch cannot avoid: q, k, v read once, o and lse written once."""
+    return wl.B * wl.H * (4 * wl.T * wl.d * 2 + 4 * wl.T)
+
+
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or the platform's processor string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def cpu_baseline_per_config(names=PER_CONFIG, budget_heads_s=3.0):
@@ -708,7 +726,10 @@ def main(argv=None):
                      "frac_at_clock": round(achieved / peak_at_clock, 4) if peak_at_clock else None,
                      "timing": "achieved = flops per launch / (one HIP event pair on the launch stream "
                                "around the timed launches / steps)",
-                     "flops_per_launch": wl.flops, **extra},
+                     "flops_per_launch": wl.flops,
+                     "compulsory_bytes": compulsory_bytes(wl),
+                     "compulsory_gbs": round(compulsory_bytes(wl) / (kern_ms * 1e-3) / 1e9, 1),
+                     **extra},
         "cpu_baseline": base,
         "parity": parity,
         "sweep": sweep,

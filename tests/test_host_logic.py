@@ -66,7 +66,14 @@ def test_bench_cpu_baseline_small():
     r, (o_ref, lse_ref), n_heads = bench.cpu_baseline(WORKLOADS["c1"], budget_s=1.0)
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["cores"] >= 1
     assert r["value"] > 0 and "heads of c1" in r["sample"]
+    assert isinstance(r["cpu_model"], str) and r["cpu_model"]
     assert n_heads == 2 and o_ref.shape == (1, 2, 256, 64) and lse_ref.shape == (1, 2, 256)
+
+
+def test_bench_compulsory_bytes():
+    # q, k, v read and o written once (bf16), lse written once (fp32): 101.4 MB at B4 H12 T4096 d64
+    assert bench.compulsory_bytes(WORKLOADS["c4"]) == 48 * (4 * 4096 * 64 * 2 + 4 * 4096) == 101449728
+    assert bench.compulsory_bytes(WORKLOADS["c5b"]) == 64 * (4 * 8192 * 128 * 2 + 4 * 8192)
 
 
 def test_bench_parity_check_uses_the_oracle_output_and_catches_errors():
