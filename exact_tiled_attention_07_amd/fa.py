@@ -224,10 +224,12 @@ def fwd_fp8(q8, k8, v8, q_descale: float, k_descale: float, v_descale: float, ca
         out = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=q8.device)
     if lse is None:
         lse = torch.empty((B, H, T), dtype=torch.float32, device=q8.device)
-    if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, H, T, d) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bfloat16 tensor [B, H, T, d]")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, T]")
+    if (out.dtype != torch.bfloat16 or tuple(out.shape) != (B, H, T, d) or not out.is_contiguous()
+            or out.device != q8.device):
+        raise ValueError("out must be a contiguous bfloat16 tensor [B, H, T, d] on q8's device")
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous()
+            or lse.device != q8.device):
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, T] on q8's device")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     with torch.cuda.device(q8.device):
         _check(lib().fa_fwd_fp8(q8.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(),
@@ -254,7 +256,7 @@ def bwd(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None, 
 
     ``o`` and ``lse`` are the outputs of ``fwd`` for the same q, k, v, causal and scale; ``dout`` is
     the gradient of the loss with respect to ``o``. All bfloat16 tensors are contiguous
-    ``[B, H, T, 64]`` on the GPU; lse is float32 ``[B, H, T]``. Returns bfloat16 gradients shaped
+    ``[B, H, T, d]`` on the GPU (d = 64 or 128); lse is float32 ``[B, H, T]``. Returns bfloat16 gradients shaped
     like q and ``delta`` float32 ``[B, H, T]`` (``dO_i . O_i``).
     """
     import torch

@@ -225,3 +225,7 @@ def test_fp8_binding_rejects():
         fa.fwd_fp8(q, q, q, 0.0, 1.0, 1.0)
     with pytest.raises(ValueError):
         fa.fwd_fp8(q, q[:, :, :4].contiguous(), q, 1.0, 1.0, 1.0)
+    with pytest.raises(ValueError):  # outputs on another device than the inputs
+        fa.fwd_fp8(q, q, q, 1.0, 1.0, 1.0, out=torch.empty(1, 1, 8, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        fa.fwd_fp8(q, q, q, 1.0, 1.0, 1.0, lse=torch.empty(1, 1, 8, dtype=torch.float32))
