@@ -263,8 +263,9 @@ def bwd(q, k, v, o, lse, dout, causal: bool = True, scale: float | None = None, 
 
     _check_inputs(q, k, v, ("o", o), ("dout", dout))
     B, H, T, d = q.shape
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, T]")
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous()
+            or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, T] on q's device")
     dq, dk, dv = _like(q, dq, "dq"), _like(q, dk, "dk"), _like(q, dv, "dv")
     delta = _like(q, delta, "delta", torch.float32, (B, H, T))
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
@@ -419,10 +420,12 @@ def merge(o_parts, lse_parts, out=None, lse=None, stream=None):
         out = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=o_parts.device)
     if lse is None:
         lse = torch.empty((B, H, T), dtype=torch.float32, device=o_parts.device)
-    if out.dtype != torch.bfloat16 or tuple(out.shape) != (B, H, T, d) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bfloat16 tensor [B, H, T, d]")
-    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 tensor [B, H, T]")
+    if (out.dtype != torch.bfloat16 or tuple(out.shape) != (B, H, T, d) or not out.is_contiguous()
+            or out.device != o_parts.device):
+        raise ValueError("out must be a contiguous bfloat16 tensor [B, H, T, d] on the parts' device")
+    if (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous()
+            or lse.device != o_parts.device):
+        raise ValueError("lse must be a contiguous float32 tensor [B, H, T] on the parts' device")
     with torch.cuda.device(o_parts.device):
         _check(lib().fa_merge(o_parts.data_ptr(), lse_parts.data_ptr(), n, out.data_ptr(),
                               lse.data_ptr(), B, H, T, d, _stream_handle(o_parts.device, stream)))

@@ -236,3 +236,5 @@ def test_bwd_binding_rejects():
         fa.bwd(q64, q64, q64, q64, lse[..., :4], q64)
     with pytest.raises(TypeError):
         fa.bwd(q64, q64, q64, q64.float(), lse, q64)
+    with pytest.raises(ValueError):  # lse on another device than q
+        fa.bwd(q64, q64, q64, q64, lse.cpu(), q64)

@@ -299,3 +299,8 @@ def test_partial_binding_rejects():
         fa.fwd_splitkv(q, k[..., :32].contiguous(), k[..., :32].contiguous())
     with pytest.raises(fa.FaError):
         fa.fwd_splitkv(q, k, k, n_splits=0)
+    parts = torch.zeros(2, 1, 1, 8, 64, device=DEV), torch.zeros(2, 1, 1, 8, device=DEV)
+    with pytest.raises(ValueError):  # merge outputs on another device than the parts
+        fa.merge(*parts, out=torch.empty(1, 1, 8, 64, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        fa.merge(*parts, lse=torch.empty(1, 1, 8, dtype=torch.float32))
