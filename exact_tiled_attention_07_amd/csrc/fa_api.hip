@@ -137,7 +137,7 @@ const TileEntry* find_tile(int d, int block_m, int block_n, int waves) {
 //   of twice the workgroups. Causal: 0.73-0.75 at nq 8 up to grid 288, 0.77-0.83 at nq 16-32 and
 //   grid 384, but 0.96 at nq 8 and grid 384 and 0.93-0.94 at grid 512. Non-causal: 0.77 at grid 96,
 //   0.91-0.95 at grid 384.
-// - 128-key tiles (234 VGPRs, two workgroups per compute unit, half the barriers and loop steps per
+// - 128-key tiles (230 VGPRs, two workgroups per compute unit, half the barriers and loop steps per
 //   key) win on short heads: causal 0.89-0.92 at grid 96-512, 0.96-0.98 at nq 8 up to grid 1536 and
 //   at nq 16 and grid 768; non-causal 0.89-0.93 at grid 384; but 1.01-1.07 at nq 4, at nq 16 and grid
 //   1536 and at nq 32 and grid 1536.
