@@ -125,6 +125,7 @@ def test_every_planted_mistake_fails_a_pin(tmp_path):
 
 PY_PINS_SPLIT = ["test_oracle_splitkv_pins.py"]
 PY_PINS_FP8 = ["test_oracle_fp8_pins.py"]
+PY_PINS_BWD = ["test_oracle_bwd_pins.py"]
 PY_MUTANTS = [
     ("merge: LSE without the max", [("lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, l)))",
                                      "lse = np.where(empty, -np.inf, np.log(np.where(empty, 1.0, l)))")],
@@ -149,6 +150,18 @@ PY_MUTANTS = [
      PY_PINS_FP8),
     ("fp8: v descale dropped", [("    v = e4m3_to_f64(v8) * vd\n    return attention_fwd_f64",
                                  "    v = e4m3_to_f64(v8)\n    return attention_fwd_f64")], PY_PINS_FP8),
+    # the row-by-row oracles used on the full-size workloads
+    ("fp8 rows: one key short", [("keys = i + 1 if causal else k.shape[0]", "keys = max(i, 1) if causal else k.shape[0]")],
+     PY_PINS_FP8),
+    ("fp8 rows: k descale dropped", [("e4m3_to_f64(k8[b, h]) * kd", "e4m3_to_f64(k8[b, h])")], PY_PINS_FP8),
+    ("bwd rows: D dropped from dQ", [("ds = p * (V[vis] @ dO[i] - D[i])", "ds = p * (V[vis] @ dO[i])")], PY_PINS_BWD),
+    ("bwd rows: key-side causal bound off by one", [("vis = idx >= j if causal else np.ones(T, dtype=bool)",
+                                                     "vis = idx > j if causal else np.ones(T, dtype=bool)")],
+     PY_PINS_BWD),
+    ("bwd rows: scale missing on dK", [("dk[n] = scale * (ds @ Q[vis])", "dk[n] = ds @ Q[vis]")], PY_PINS_BWD),
+    ("bwd rows: statistics mask off by one", [("s = np.where(idx[None, :kend] > idx[i0:i1, None], -np.inf, s)",
+                                               "s = np.where(idx[None, :kend] >= idx[i0:i1, None], -np.inf, s)")],
+     PY_PINS_BWD),
 ]
 
 
@@ -179,7 +192,7 @@ def run_pins_in_tree(root, pins):
 def test_every_planted_mistake_in_the_numpy_oracle_fails_a_pin(tmp_path):
     control = str(tmp_path / "control")
     copy_tree(control)
-    rc, out = run_pins_in_tree(control, PY_PINS_SPLIT + PY_PINS_FP8)
+    rc, out = run_pins_in_tree(control, PY_PINS_SPLIT + PY_PINS_FP8 + PY_PINS_BWD)
     assert rc == 0, out
     trees = []
     for n, (name, edits, pins) in enumerate(PY_MUTANTS):
