@@ -6,7 +6,7 @@ import pytest
 
 import bench
 from exact_tiled_attention_07_amd.inputs import WORKLOADS, bf16_bits_from_f32, bf16_bits_to_f32
-from parity import O_TOL, bf16_ulp, compare
+from parity import O_TOL, bf16_ulp, compare, passed
 
 
 def test_bench_refuses_more_than_one_gpu(capsys):
@@ -127,6 +127,14 @@ def test_tolerance_reading():
     # 0.014 literal; 0.0155 <= ulp(3)=2^-6; 0.031 <= ulp(5)=2^-5; 0.032 > 2^-5 fails; 0.016 at |1| fails
     assert s["n_ulp_clause"] == 2 and s["n_fail_o"] == 2
     assert math.isclose(O_TOL, 1.5e-2)
+    # LSE: the literal 1e-3, in both directions; a non-finite output fails and is counted
+    lse_ref = np.array([2.0, -3.0, 10.0])
+    s = compare(np.ones(3), lse_ref + np.array([9.9e-4, -9.9e-4, 0.0]), np.ones(3), lse_ref)
+    assert s["n_fail_lse"] == 0 and passed(s)
+    s = compare(np.ones(3), lse_ref + np.array([1.01e-3, 0.0, -1.01e-3]), np.ones(3), lse_ref)
+    assert s["n_fail_lse"] == 2 and not passed(s)
+    s = compare(np.array([1.0, np.nan, np.inf]), lse_ref, np.ones(3), lse_ref)
+    assert s["n_nonfinite"] == 2 and s["n_fail_o"] == 2 and not passed(s)
 
 
 def test_page_claims_are_context_only():
