@@ -7,6 +7,7 @@ import ctypes
 import json
 import os
 
+import numpy as np
 import pytest
 
 from exact_tiled_attention_07_amd import fa
@@ -190,6 +191,11 @@ def test_plan_head_groups():
              (0, 8, 1000, 64, True, 1)]       # no heads: nothing is launched, the plan says 1
     for B, H, T, d, causal, want in cases:
         assert hg(B, H, T, d, causal) == want == expect(B, H, T, d, causal), (B, H, T, d, causal)
+    rng = np.random.default_rng(8)  # and a seeded sweep of shapes against the rule as written above
+    for _ in range(500):
+        B, H = int(rng.integers(1, 9)), int(rng.integers(1, 65))
+        T, d, causal = int(rng.integers(1, 1 << 17)), int(rng.choice([64, 128])), bool(rng.integers(0, 2))
+        assert hg(B, H, T, d, causal) == expect(B, H, T, d, causal), (B, H, T, d, causal)
 
 
 def test_plan_errors():
