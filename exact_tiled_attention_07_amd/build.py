@@ -24,9 +24,12 @@ def hipcc() -> str:
     return os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc")
 
 
-def build(extra_flags=(), out: str = LIB, src: str = SRC) -> str:
+def build(extra_flags=(), out: str = LIB, src: str = SRC, mfma_vgpr_form: bool = True) -> str:
+    """mfma_vgpr_form=False leaves the choice of MFMA accumulator registers to the compiler, which
+    takes VGPRs in a kernel that uses no AGPRs and AGPRs in one that does."""
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra_flags, "-I", os.path.join(ROOT, "include"),
+    flags = [f for f in HIPCC_FLAGS if mfma_vgpr_form or f not in ("-mllvm", "-amdgpu-mfma-vgpr-form")]
+    cmd = [hipcc(), *flags, *extra_flags, "-I", os.path.join(ROOT, "include"),
            "-I", os.path.join(PKG, "csrc"), src, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature for this target"
@@ -50,8 +53,9 @@ ISSUE_LIB = os.path.join(ROOT, "tests", "libissue_rate_probe.so")
 
 def build_probe() -> str:
     """Test infrastructure: the probes the GPU tests run (the FP8 matrix instruction's accuracy, and
-    the issue rates of the forward's inner-loop instructions)."""
-    build(out=ISSUE_LIB, src=ISSUE_SRC)
+    the issue rates of the forward's inner-loop instructions; one of its modes compares the matrix
+    accumulators in AGPRs with the VGPRs that every other mode and the library use)."""
+    build(out=ISSUE_LIB, src=ISSUE_SRC, mfma_vgpr_form=False)
     return build(out=PROBE_LIB, src=PROBE_SRC)
 
 

@@ -4,8 +4,12 @@ the measured basis of the d = 64 forward's per-tile cycle budget.
 Per SIMD, in cycles, with the SIMD's own elapsed time (its slowest wave): the MFMA 32x32x16 bf16
 takes 32 cycles at every occupancy; v_exp_f32 issues at about a third of the rate of v_fma_f32; and
 the softmax's minimal instruction mix for one 64-key tile at d = 64 (about 9 VALU instructions per
-MFMA) keeps the SIMD busy well beyond the MFMA time, more so with the fragment reads from LDS. These
-are the facts the kernel's design notes rely on; the test asserts them loosely and prints the table.
+MFMA) keeps the SIMD busy well beyond the MFMA time, more so with the fragment reads from LDS. The
+MFMAs do not hide wholly behind the VALU work of the other waves: each one adds to the time of the
+mix alone, more for two 16x16x32 instructions than for one 32x32x16 of the same flops, and the same
+with the accumulators in AGPRs. The FP8 forward's conversion of its weights, v_cvt_pk_fp8_f32,
+issues at the rate of v_exp_f32. These are the facts the kernels' design notes rely on; the test
+asserts them loosely and prints the table.
 """
 import ctypes
 import os
@@ -18,7 +22,9 @@ PROBE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libissue_rate_
 ITERS = 2000
 MODES = {0: "16 fma", 1: "16 exp", 2: "16 add", 3: "16 max3", 4: "16 cvt_pk_bf16", 5: "4 mfma",
          6: "4 mfma + softmax mix (37 VALU)", 7: "mode 6 + 6 LDS reads", 8: "mode 6 + 3 LDS reads",
-         9: "two roles: 4 mfma | 37 VALU"}
+         9: "two roles: 4 mfma | 37 VALU", 10: "the 37 VALU alone", 11: "16 cvt_pk_fp8",
+         12: "2 fp8 mfma (128 cycles) + 37 VALU", 13: "8 mfma 16x16x32 + 37 VALU",
+         14: "mode 6, accumulators in AGPRs", 15: "2 fp8 mfma 32x32x64"}
 
 
 @pytest.fixture(scope="module")
@@ -63,3 +69,22 @@ def test_softmax_mix_caps_the_mfma(cycles):
         assert cycles[(7, w)] > cycles[(6, w)]
     # splitting the same work into MFMA-only and VALU-only waves is not faster
     assert cycles[(9, 4)] > cycles[(6, 4)]
+
+
+def test_mfma_adds_to_the_mix(cycles):
+    for w in (3, 4):
+        # the mix alone takes longer than its 4 MFMAs, and the MFMAs still add to it
+        assert cycles[(10, w)] > 128.0
+        assert cycles[(6, w)] > cycles[(10, w)] + 4 * 5.0
+        # the same flops in twice the instructions (16x16x32) cost more ...
+        assert cycles[(13, w)] > cycles[(6, w)]
+        # ... and the same 128 MFMA cycles in half the instructions (FP8 32x32x64) no more
+        assert cycles[(12, w)] < cycles[(6, w)] * 1.03
+        # accumulators in AGPRs instead of VGPRs change nothing for the better
+        assert cycles[(14, w)] > cycles[(6, w)] * 0.97
+
+
+def test_fp8_conversion_issues_like_exp(cycles):
+    assert cycles[(15, 4)] == pytest.approx(128.0, rel=0.03)  # 64 cycles per FP8 32x32x64
+    assert cycles[(11, 4)] > 1.5 * cycles[(4, 4)]
+    assert cycles[(11, 4)] == pytest.approx(cycles[(1, 4)], rel=0.2)
