@@ -16,13 +16,18 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
     """List the recorded parity statistics (literal max errors, elements admitted only by the
     one-ulp clause) at the end of the run, so that they survive a quiet (-q) run's output."""
     try:
-        from parity import RECORDED
+        from parity import BWD_RECORDED, RECORDED
     except ImportError:
         return
-    if not RECORDED:
-        return
-    terminalreporter.section("parity against the oracle (rows compared in full)")
-    for label, s in RECORDED:
-        terminalreporter.write_line(
-            f"{label}: n={s['n']} max|dO|={s['max_err_o']:.4e} max|dLSE|={s['max_err_lse']:.3e} "
-            f"ulp_clause={s['n_ulp_clause']} fail={s['n_fail_o'] + s['n_fail_lse']}")
+    if RECORDED:
+        terminalreporter.section("parity against the oracle (rows compared in full)")
+        for label, s in RECORDED:
+            terminalreporter.write_line(
+                f"{label}: n={s['n']} max|dO|={s['max_err_o']:.4e} max|dLSE|={s['max_err_lse']:.3e} "
+                f"ulp_clause={s['n_ulp_clause']} fail={s['n_fail_o'] + s['n_fail_lse']}")
+    if BWD_RECORDED:
+        terminalreporter.section("backward against the oracle (every element; worst |error| / "
+                                 "(|ref| + head rms), then rms error / rms)")
+        for label, grads in BWD_RECORDED:
+            terminalreporter.write_line(f"{label}: " + " ".join(
+                f"{n} {s['max_ratio']:.4f}/{s['rms_ratio']:.4f}" for n, s in grads.items()))

@@ -26,6 +26,7 @@ import exact_tiled_attention_07_amd as fa
 from exact_tiled_attention_07_amd.inputs import WORKLOADS, bf16_bits_from_f32, bf16_bits_to_f32, make_qkv, to_torch_bf16
 
 from bwd_rounding_model import grad_stats
+from parity import record_bwd
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +58,7 @@ def run_gpu(qb, kb, vb, dob, causal, scale):
     return [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv, delta)]
 
 
-def check(qb, kb, vb, dob, causal, scale, label):
+def check(qb, kb, vb, dob, causal, scale, label, keep=False):
     say(f"[gpu bwd] {label} shape={qb.shape} causal={causal} scale={scale}")
     got = run_gpu(qb, kb, vb, dob, causal, scale)
     ref = oracle.attention_bwd(qb, kb, vb, dob, causal, scale)
@@ -69,6 +70,8 @@ def check(qb, kb, vb, dob, causal, scale, label):
     stats = {n: grad_tolerance(n, g, r, a) for n, g, r, a in zip(("dq", "dk", "dv", "delta"), got, ref, floors)}
     say(f"[gpu bwd] {label} " + " ".join(f"{n}: {s['max_ratio']:.4f}/{s['rms_ratio']:.4f}"
                                          for n, s in stats.items()))
+    if keep:
+        record_bwd(label, stats)
     return got, ref
 
 
@@ -101,7 +104,16 @@ def test_bwd_configs(name):
     wl = WORKLOADS[name]
     qb, kb, vb = wl.make()
     dob, _, _ = make_qkv(wl.B, wl.H, wl.T, wl.d, seed=wl.seed + 7919)
-    check(qb, kb, vb, dob, wl.causal, wl.scale, wl.name)
+    check(qb, kb, vb, dob, wl.causal, wl.scale, wl.name, keep=True)
+
+
+def test_bwd_c4_every_element():
+    # the backward as the bench times it: all 48 heads of the causal T = 4096 workload (its sigma-2
+    # inputs), dO drawn from the workload's seed + 7919; every element of dQ, dK, dV and D
+    wl = WORKLOADS["c4"]
+    qb, kb, vb = wl.make()
+    dob, _, _ = make_qkv(wl.B, wl.H, wl.T, wl.d, seed=wl.seed + 7919)
+    check(qb, kb, vb, dob, wl.causal, wl.scale, f"{wl.name} (every element)", keep=True)
 
 
 def test_bwd_long_sequence():
