@@ -42,40 +42,12 @@ from exact_tiled_attention_07_amd.inputs import WORKLOADS, make_qkv_fp8
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-from fp8_mfma import EPS_MFMA_PV, EPS_MFMA_QK  # noqa: E402  (measured: test_fp8_mfma_accuracy_gpu.py)
+from fp8_bounds import error_model_heads, error_model_rows  # noqa: E402
 MSE_FACTOR = 3.0
 
 
 def say(msg):
     print(msg, flush=True)
-
-
-def error_model(q8, k8, v8, scales, causal, scale, heads_rows):
-    """Per selected row: the element bound on O, the bound on LSE and the predicted squared error of O
-    (numpy float64). heads_rows: list of (b, h, i)."""
-    qd, kd, vd = (float(np.float32(s)) for s in scales)
-    bounds, lbounds, pred = [], [], []
-    cache = {}
-    for b, h, i in heads_rows:
-        if (b, h) not in cache:
-            cache[(b, h)] = (oracle.e4m3_to_f64(q8[b, h]) * qd, oracle.e4m3_to_f64(k8[b, h]) * kd,
-                             oracle.e4m3_to_f64(v8[b, h]) * vd)
-        qf, kf, vf = cache[(b, h)]
-        keys = i + 1 if causal else kf.shape[0]
-        s = scale * (kf[:keys] @ qf[i])
-        ds = EPS_MFMA_QK * scale * float((np.abs(kf[:keys]) @ np.abs(qf[i])).max())
-        e = np.exp(s - s.max())
-        L = e.sum()
-        p = e / L
-        av = np.abs(vf[:keys])
-        W = p @ av
-        o = p @ vf[:keys]
-        lse = s.max() + np.log(L)
-        bounds.append(2.0 ** -4 * W + 2.0 ** -18 * av.sum(axis=0) / L + 2.0 ** -9 * np.abs(o)
-                      + (1e-3 + EPS_MFMA_PV + 2 * ds) * W + 1e-6)
-        lbounds.append(ds + 1e-5 + 1e-6 * abs(lse))
-        pred.append(2.0 ** -8 / 6 * ((p ** 2) @ (vf[:keys] ** 2)) + (2.0 ** -9 * o) ** 2 / 3)
-    return np.array(bounds), np.array(lbounds), np.array(pred)
 
 
 def run_gpu(q8, k8, v8, scales, causal, scale):
@@ -86,20 +58,21 @@ def run_gpu(q8, k8, v8, scales, causal, scale):
 
 
 def check(q8, k8, v8, scales, causal, scale, label, rows=None):
+    """rows=None: every row, against the whole-head oracle (bounds from whole-head products);
+    else the listed (b, h, i) rows, against the oracle's row entry."""
     B, H, T, d = q8.shape
     say(f"[gpu fp8] {label} shape={q8.shape} causal={causal} scale={scale}")
     o, lse = run_gpu(q8, k8, v8, scales, causal, scale)
     if rows is None:
         o_ref, lse_ref = oracle.attention_fwd_fp8(q8, k8, v8, causal, scale, *scales)
-        rows = [(b, h, i) for b in range(B) for h in range(H) for i in range(T)]
-        o_ref = o_ref.reshape(-1, d)
-        lse_ref = lse_ref.reshape(-1)
+        o_ref, lse_ref = o_ref.reshape(-1, d), lse_ref.reshape(-1)
+        bound, lbound, pred = (x.reshape(-1, d) if x.ndim == 4 else x.reshape(-1)
+                               for x in error_model_heads(q8, k8, v8, scales, causal, scale))
+        got_o, got_l = o.reshape(-1, d), lse.reshape(-1)
     else:
-        o_ref = None  # the oracle's row entry, below
-    bound, lbound, pred = error_model(q8, k8, v8, scales, causal, scale, rows)
-    got_o = np.stack([o[b, h, i] for b, h, i in rows])
-    got_l = np.array([lse[b, h, i] for b, h, i in rows])
-    if o_ref is None:
+        bound, lbound, pred = error_model_rows(q8, k8, v8, scales, causal, scale, rows)
+        got_o = np.stack([o[b, h, i] for b, h, i in rows])
+        got_l = np.array([lse[b, h, i] for b, h, i in rows])
         o_ref, lse_ref = oracle.attention_fwd_fp8_rows(q8, k8, v8, causal, scale, *scales, rows)
     err = np.abs(got_o - o_ref)
     lerr = np.abs(got_l - lse_ref)
@@ -125,6 +98,14 @@ def test_fp8_configs(name):
     wl = WORKLOADS[name]
     q8, k8, v8, scales = make_qkv_fp8(wl.B, wl.H, wl.T, wl.d, wl.seed, wl.sigma)
     check(q8, k8, v8, scales, wl.causal, wl.scale, wl.name + " fp8")
+
+
+def test_fp8_c4_every_row():
+    # the FP8 forward as the bench times it on the causal T = 4096 workload (E4M3 copies of its
+    # sigma-2 inputs): all 48 heads, every row
+    wl = WORKLOADS["c4"]
+    q8, k8, v8, scales = make_qkv_fp8(wl.B, wl.H, wl.T, wl.d, wl.seed, wl.sigma)
+    check(q8, k8, v8, scales, wl.causal, wl.scale, wl.name + " fp8 (every row)")
 
 
 @pytest.mark.parametrize("name", ["c4", "c5a", "c5b"])
@@ -168,7 +149,7 @@ def test_fp8_causal_head_groups():
                    for i in [0, 1, 63, 64, T // 2, T - 1] + rng.integers(0, T, 6).tolist()})
     got_o = np.stack([o[b, h, i].float().cpu().numpy().astype(np.float64) for b, h, i in rows])
     got_l = np.array([float(lse[b, h, i]) for b, h, i in rows])
-    bound, lbound, pred = error_model(q8, k8, v8, scales, True, 0.125, rows)
+    bound, lbound, pred = error_model_rows(q8, k8, v8, scales, True, 0.125, rows)
     o_ref, lse_ref = oracle.attention_fwd_fp8_rows(q8, k8, v8, True, 0.125, *scales, rows)
     err, lerr = np.abs(got_o - o_ref), np.abs(got_l - lse_ref)
     say(f"[gpu fp8] head groups max ratio to bound {(err / bound).max():.3f} lse ratio {(lerr / lbound).max():.3f}")
