@@ -246,18 +246,6 @@ def time_backward(wl, steps, warmup):
     return ev_ms, {"wall_ms": wall_ms}
 
 
-def sparse_mask(T, density, seed):
-    """The bench's block mask: each 128x64 block kept with probability `density`, plus the blocks
-    on the diagonal (so every query sees a key)."""
-    import numpy as np
-
-    nq, nk = -(-T // 128), -(-T // 64)
-    m = (np.random.Generator(np.random.PCG64(seed)).random((1, nq, nk)) < density).astype(np.uint8)
-    for i in range(nq):
-        m[0, i, 2 * i:min(nk, 2 * i + 2)] = 1
-    return m
-
-
 def visible_pairs(mask, T, causal):
     """Number of (query, key) pairs a block mask leaves visible (per head)."""
     import numpy as np
@@ -281,7 +269,7 @@ def time_sparse(wl, steps, warmup, density=0.25):
     import torch
 
     import exact_tiled_attention_07_amd as fa
-    from exact_tiled_attention_07_amd.inputs import to_torch_bf16
+    from exact_tiled_attention_07_amd.inputs import sparse_mask, to_torch_bf16
 
     dev = torch.device("cuda:0")
     q, k, v = (to_torch_bf16(x, dev) for x in wl.make())

@@ -47,6 +47,17 @@ def make_qkv(B: int, H: int, T: int, d: int, seed: int, sigma: float = 1.0):
     return tuple(out)
 
 
+def sparse_mask(T: int, density: float, seed: int) -> np.ndarray:
+    """A block mask for the block-sparse forward, uint8 [1, ceil(T/128), ceil(T/64)] (one mask for
+    every head): each 128 x 64 block kept when a PCG64(seed) uniform draw is below `density`, plus
+    the two blocks on each query block's diagonal, so that every query sees a key."""
+    nq, nk = -(-T // 128), -(-T // 64)
+    m = (np.random.Generator(np.random.PCG64(seed)).random((1, nq, nk)) < density).astype(np.uint8)
+    for i in range(nq):
+        m[0, i, 2 * i:min(nk, 2 * i + 2)] = 1
+    return m
+
+
 def to_torch_bf16(bits, device="cpu"):
     """View uint16 bf16 bit patterns as a torch bfloat16 tensor on ``device`` (no rounding)."""
     import torch

@@ -3,7 +3,7 @@ import numpy as np
 import torch
 
 from exact_tiled_attention_07_amd.inputs import (WORKLOADS, bf16_bits_from_f32, bf16_bits_to_f32,
-                                                 make_qkv, to_torch_bf16)
+                                                 make_qkv, to_torch_bf16, sparse_mask)
 
 
 def test_rne_matches_torch_cast():
@@ -48,3 +48,18 @@ def test_workload_table():
     w = WORKLOADS["c3"]
     assert w.flops == 2.0 * 4 * 12 * 1024 * 1024 * 64
     assert abs(WORKLOADS["c5b"].flops - 4.0 * 4 * 16 * 8192 ** 2 * 128) < 1
+
+
+def test_sparse_mask():
+    # the block-sparse workload's mask: one mask for every head, 128 x 64 blocks, the two diagonal
+    # blocks of every query block set, the rest kept at the given density, the same for a seed
+    m = sparse_mask(16384, 0.25, 5)
+    assert m.shape == (1, 128, 256) and m.dtype == np.uint8 and set(np.unique(m)) <= {0, 1}
+    for i in range(128):
+        assert m[0, i, 2 * i] == 1 and m[0, i, 2 * i + 1] == 1
+    assert 0.24 < m.mean() < 0.27
+    np.testing.assert_array_equal(m, sparse_mask(16384, 0.25, 5))
+    assert not np.array_equal(m, sparse_mask(16384, 0.25, 6))
+    # a ragged length: the last query block's diagonal ends at the last key block
+    r = sparse_mask(1000, 0.0, 1)
+    assert r.shape == (1, 8, 16) and r[0, 7, 14] == 1 and r[0, 7, 15] == 1 and r.sum() == 16

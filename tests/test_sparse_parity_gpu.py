@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import exact_tiled_attention_07_amd as fa
-from exact_tiled_attention_07_amd.inputs import make_qkv, to_torch_bf16
+from exact_tiled_attention_07_amd.inputs import WORKLOADS, make_qkv, sparse_mask, to_torch_bf16
 
 from parity import assert_parity, compare
 
@@ -94,6 +94,14 @@ def test_sparse_long_sequence():
     for i in range(mask.shape[1]):
         mask[0, i, 2 * i:2 * i + 2] = 1
     check(qb, kb, vb, mask, True, 0.125, "T=16384")
+
+
+def test_sparse_bench_workload_every_row():
+    # the block-sparse forward as the bench times it: all 48 heads of the causal T = 16384 workload
+    # with its mask (25% of the 128 x 64 blocks plus the diagonal ones, seed 5), every row
+    wl = WORKLOADS["c5a"]
+    qb, kb, vb = wl.make()
+    check(qb, kb, vb, sparse_mask(wl.T, 0.25, wl.seed), wl.causal, wl.scale, wl.name + " sparse 25%")
 
 
 def test_sparse_head_groups():
