@@ -9,6 +9,7 @@ spacing is 2^-5, so even the correctly rounded exact answer can sit 1.5625e-2 aw
 clause admits exactly the two bf16 neighbours of the exact value (and nothing farther). The
 literal max error and the number of elements that needed the ulp clause are reported.
 Tolerance on LSE (fp32): |LSE_gpu - LSE_ref| <= 1e-3.
+``compare`` also reports the RMS of the O error and of O_ref, for the tests' relative RMS check.
 """
 from __future__ import annotations
 
@@ -40,6 +41,8 @@ def compare(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray, lse_ref: 
         "n_fail_lse": int(np.count_nonzero(~(lerr <= LSE_TOL))),
         "n_nonfinite": int(np.count_nonzero(~np.isfinite(o_gpu)) + np.count_nonzero(~np.isfinite(lse_gpu))),
         "n": int(err.size),
+        "rms_err_o": float(np.sqrt(np.mean(err ** 2))) if err.size else 0.0,
+        "rms_ref_o": float(np.sqrt(np.mean(np.square(o_ref)))) if err.size else 0.0,
     }
 
 

@@ -24,7 +24,8 @@ def pytest_terminal_summary(terminalreporter, exitstatus, config):
         for label, s in RECORDED:
             terminalreporter.write_line(
                 f"{label}: n={s['n']} max|dO|={s['max_err_o']:.4e} max|dLSE|={s['max_err_lse']:.3e} "
-                f"ulp_clause={s['n_ulp_clause']} fail={s['n_fail_o'] + s['n_fail_lse']}")
+                f"ulp_clause={s['n_ulp_clause']} fail={s['n_fail_o'] + s['n_fail_lse']} "
+                f"rms|dO|/rms|O|={s['rms_err_o'] / max(s['rms_ref_o'], 1e-300):.2e}")
     if BWD_RECORDED:
         terminalreporter.section("backward against the oracle (every element; worst |error| / "
                                  "(|ref| + head rms), then rms error / rms)")

@@ -4,9 +4,9 @@ Per output row i of one head, with the decoded, descaled values q, k, v, the vis
 weights p_j = softmax_j(scale q_i . k_j), L = sum_j exp(s_j - max s), W_c = sum_j p_j |v_jc| and
 dS_i = EPS_MFMA_QK * scale * max_j sum_c |q_ic k_jc|:
 
-    bound_c = 2^-4 W_c + 2^-18 sum_j |v_jc| / L + 2^-9 |O_c| + (1e-3 + EPS_MFMA_PV + 2 dS_i) W_c + 1e-6
+    bound_c = 2^-4 W_c + 2^-18 sum_j |v_jc| / L + 2^-8 |O_c| + (1e-3 + EPS_MFMA_PV + 2 dS_i) W_c + 1e-6
     lse bound = dS_i + 1e-5 + 1e-6 |LSE|
-    predicted squared error_c = 2^-8 / 6 sum_j p_j^2 v_jc^2 + (2^-9 O_c)^2 / 3
+    predicted squared error_c = 2^-8 / 6 sum_j p_j^2 v_jc^2 + 2^-16 / 6 O_c^2
 
 ``error_model_rows`` evaluates them row by row for selected rows; ``error_model_heads`` evaluates the
 same formulas for every row of every head with whole-head matrix products (a CPU test checks that
@@ -43,10 +43,10 @@ def error_model_rows(q8, k8, v8, scales, causal, scale, heads_rows):
         W = p @ av
         o = p @ vf[:keys]
         lse = s.max() + np.log(L)
-        bounds.append(2.0 ** -4 * W + 2.0 ** -18 * av.sum(axis=0) / L + 2.0 ** -9 * np.abs(o)
+        bounds.append(2.0 ** -4 * W + 2.0 ** -18 * av.sum(axis=0) / L + 2.0 ** -8 * np.abs(o)
                       + (1e-3 + EPS_MFMA_PV + 2 * ds) * W + 1e-6)
         lbounds.append(ds + 1e-5 + 1e-6 * abs(lse))
-        pred.append(2.0 ** -8 / 6 * ((p ** 2) @ (vf[:keys] ** 2)) + (2.0 ** -9 * o) ** 2 / 3)
+        pred.append(2.0 ** -8 / 6 * ((p ** 2) @ (vf[:keys] ** 2)) + 2.0 ** -16 / 6 * o ** 2)
     return np.array(bounds), np.array(lbounds), np.array(pred)
 
 
@@ -79,9 +79,9 @@ def error_model_heads(q8, k8, v8, scales, causal, scale):
             o = p @ vf
             lse = m + np.log(L)
             sum_av = np.cumsum(av, axis=0) if causal else np.broadcast_to(av.sum(axis=0), (T, d))
-            bound[b, h] = (2.0 ** -4 * W + 2.0 ** -18 * sum_av / L[:, None] + 2.0 ** -9 * np.abs(o)
+            bound[b, h] = (2.0 ** -4 * W + 2.0 ** -18 * sum_av / L[:, None] + 2.0 ** -8 * np.abs(o)
                            + (1e-3 + EPS_MFMA_PV + 2 * ds[:, None]) * W + 1e-6)
             lbound[b, h] = ds + 1e-5 + 1e-6 * np.abs(lse)
             p *= p
-            pred[b, h] = 2.0 ** -8 / 6 * (p @ (vf ** 2)) + (2.0 ** -9 * o) ** 2 / 3
+            pred[b, h] = 2.0 ** -8 / 6 * (p @ (vf ** 2)) + 2.0 ** -16 / 6 * o ** 2
     return bound, lbound, pred

@@ -6,9 +6,9 @@ p'_j = 2^8 exp(s_j - m) to E4M3 before the second product: a relative error of a
 p'_j >= 2^-6 and an absolute error of at most 2^-10 below (the subnormal spacing is 2^-9). With
 l' = sum p'_j = 2^8 L and W_c = sum_j p_j |v_jc| (p normalised), each output element obeys
 
-    |O_gpu - O| <= 2^-4 W_c + 2^-18 sum_j |v_jc| / L + 2^-9 |O| + 1e-3 W_c + 1e-6,
+    |O_gpu - O| <= 2^-4 W_c + 2^-18 sum_j |v_jc| / L + 2^-8 |O| + 1e-3 W_c + 1e-6,
 
-where 2^-9 |O| is the final bf16 rounding and 1e-3 W_c covers fp32 accumulation over up to 16384
+where 2^-8 |O| is the final bf16 rounding (8 significant bits) and 1e-3 W_c covers fp32 accumulation over up to 16384
 terms (n u = 16384 x 6e-8) and the fp32 score factor.
 
 The FP8 MFMA does not add its 64 products exactly in fp32: it truncates products far below the
@@ -26,7 +26,7 @@ element by element.
 It is loose because rounding errors cancel, so the mean square error is also checked against its
 expectation: RNE to 3 mantissa bits has E[rel^2] = 2^-8 / 6 (relative error uniform within half an
 ulp, mantissa fraction uniform), so E[(O_gpu - O)_c^2] = 2^-8 / 6 sum_j p_j^2 v_jc^2 (+ the bf16
-term); the measured mean over all elements must stay below 3 times the predicted mean. LSE uses the
+rounding's 2^-16 / 6 O_c^2, the same formula at 7 mantissa bits); the measured mean over all elements must stay below 3 times the predicted mean. LSE uses the
 fp32 weights (not the rounded ones): its error is that of the scores.
 """
 import math

@@ -140,3 +140,27 @@ def test_tolerance_reading():
 def test_page_claims_are_context_only():
     assert bench.PAGE_CLAIMS and all({"claim", "hardware", "source"} <= set(c) for c in bench.PAGE_CLAIMS)
     assert not any("MI355X" == c["hardware"] for c in bench.PAGE_CLAIMS)
+
+
+def test_rms_check_matches_two_bf16_roundings():
+    # the relative RMS allowance of the forward tests is twice the expected error of the kernel's two
+    # bf16 roundings (P before P.V, O at the end) for i.i.d. zero-mean V: 2^-7 / sqrt(12). Simulate
+    # exactly those roundings in float64 on causal rows of random scores and check the expectation
+    from parity import RMS_O_REL
+
+    rng = np.random.default_rng(12)
+    T, d = 512, 64
+    s = rng.standard_normal((T, T)) * 2.0
+    s[np.triu_indices(T, 1)] = -np.inf
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    l = p.sum(axis=1, keepdims=True)
+    v = bf16_bits_to_f32(bf16_bits_from_f32(rng.standard_normal((T, d)).astype(np.float32))).astype(np.float64)
+    o = (p @ v) / l
+    p16 = bf16_bits_to_f32(bf16_bits_from_f32(p.astype(np.float32))).astype(np.float64)
+    o16 = bf16_bits_to_f32(bf16_bits_from_f32(((p16 @ v) / l).astype(np.float32))).astype(np.float64)
+    rel = np.sqrt(np.mean((o16 - o) ** 2) / np.mean(o ** 2))
+    o_only = np.sqrt(np.mean((bf16_bits_to_f32(bf16_bits_from_f32(o.astype(np.float32))) - o) ** 2)
+                     / np.mean(o ** 2))
+    assert o_only == pytest.approx(2.0 ** -7 / 24 ** 0.5, rel=0.05)  # the rounding of O alone
+    assert o_only < rel <= 1.02 * 2.0 ** -7 / 12 ** 0.5                 # P's adds at most as much
+    assert rel <= RMS_O_REL / 1.9

@@ -17,7 +17,7 @@ import oracle
 import exact_tiled_attention_07_amd as fa
 from exact_tiled_attention_07_amd.inputs import WORKLOADS, bf16_bits_from_f32, bf16_bits_to_f32, make_qkv, to_torch_bf16
 
-from parity import assert_parity, compare, record
+from parity import assert_parity, assert_rms, compare, record
 
 pytestmark = pytest.mark.gpu
 
@@ -72,6 +72,7 @@ def test_configs_full(name):
     qb, kb, vb = wl.make()
     o, _, stats = full_check(qb, kb, vb, wl.causal, wl.scale, wl.name)
     record(wl.name, stats)
+    assert_rms(stats, wl.name)
     # causal row 0 sees only key 0: exp2(0) = 1, masked p = 0, so O[0] is V[0] bit for bit
     np.testing.assert_array_equal(o[:, :, 0, :], bf16_bits_to_f32(vb)[:, :, 0, :])
     assert stats["n_ulp_clause"] == 0
@@ -111,6 +112,7 @@ def test_configs_every_row(name, h0, h1):
     say(f"[gpu] {label} {stats}")
     record(label, stats)
     assert_parity(stats, label)
+    assert_rms(stats, label)
     if wl.causal:  # row 0 sees only key 0: O[0] is V[0] bit for bit
         np.testing.assert_array_equal(o_g[:, :, 0, :], bf16_bits_to_f32(flat[2])[:, :, 0, :])
     if wl.sigma == 1.0:  # N(0,1) inputs keep |O| < 2: the literal bound alone must hold

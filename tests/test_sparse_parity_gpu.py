@@ -15,7 +15,7 @@ import oracle
 import exact_tiled_attention_07_amd as fa
 from exact_tiled_attention_07_amd.inputs import WORKLOADS, make_qkv, sparse_mask, to_torch_bf16
 
-from parity import assert_parity, compare
+from parity import assert_parity, assert_rms, compare
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +39,7 @@ def run_sparse(qb, kb, vb, mask, causal, scale):
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def check(qb, kb, vb, mask, causal, scale, label):
+def check(qb, kb, vb, mask, causal, scale, label, rms=False):
     say(f"[gpu sparse] {label} shape={qb.shape} causal={causal} mask={mask.shape} density={mask.mean():.2f}")
     o, lse = run_sparse(qb, kb, vb, mask, causal, scale)
     o_ref, lse_ref = oracle.attention_fwd_blockmask(qb, kb, vb, causal, scale, mask, 128, 64)
@@ -50,6 +50,8 @@ def check(qb, kb, vb, mask, causal, scale, label):
     stats = compare(o[live], lse[live], o_ref[live], lse_ref[live])
     say(f"[gpu sparse] {label} {stats} empty rows {int(empty.sum())}")
     assert_parity(stats, label)
+    if rms:  # i.i.d. zero-mean V over many rows: the relative RMS check too
+        assert_rms(stats, label)
     return o, lse
 
 
@@ -101,7 +103,7 @@ def test_sparse_bench_workload_every_row():
     # with its mask (25% of the 128 x 64 blocks plus the diagonal ones, seed 5), every row
     wl = WORKLOADS["c5a"]
     qb, kb, vb = wl.make()
-    check(qb, kb, vb, sparse_mask(wl.T, 0.25, wl.seed), wl.causal, wl.scale, wl.name + " sparse 25%")
+    check(qb, kb, vb, sparse_mask(wl.T, 0.25, wl.seed), wl.causal, wl.scale, wl.name + " sparse 25%", rms=True)
 
 
 def test_sparse_head_groups():

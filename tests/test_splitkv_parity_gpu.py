@@ -20,7 +20,7 @@ import oracle
 import exact_tiled_attention_07_amd as fa
 from exact_tiled_attention_07_amd.inputs import WORKLOADS, make_partials, make_qkv, to_torch_bf16
 
-from parity import assert_parity, compare, record
+from parity import assert_parity, assert_rms, compare, record
 
 pytestmark = pytest.mark.gpu
 
@@ -188,6 +188,7 @@ def test_split_long_sequence_every_row(h0, h1):
     say(f"[gpu splitkv] {label} {stats}")
     record(label, stats)
     assert_parity(stats, label)
+    assert_rms(stats, label)
     assert stats["n_ulp_clause"] == 0  # N(0,1) inputs keep |O| < 2
 
 
