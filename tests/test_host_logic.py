@@ -114,7 +114,7 @@ def test_bf16_ulp_is_the_spacing_of_bf16():
     # the next bf16 value above |x| (for x on the bf16 grid) is |x| + ulp
     for xi, ui in zip(np.abs(x), ulp):
         b = bf16_bits_from_f32(np.float32(xi))
-        nxt = bf16_bits_to_f32(np.uint16(int(b) + 1))
+        nxt = bf16_bits_to_f32(np.uint16(int(np.asarray(b).reshape(-1)[0]) + 1))
         if bf16_bits_to_f32(b) == np.float32(xi):
             assert nxt - xi == pytest.approx(ui)
     assert ulp[0] == 2.0 ** -7 and ulp[4] == 2.0 ** -5 and ulp[6] == 2.0 ** -4
