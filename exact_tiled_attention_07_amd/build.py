@@ -49,13 +49,16 @@ PROBE_LIB = os.path.join(ROOT, "tests", "libfp8_mfma_probe.so")
 
 ISSUE_SRC = os.path.join(ROOT, "tests", "issue_rate_probe.hip")
 ISSUE_LIB = os.path.join(ROOT, "tests", "libissue_rate_probe.so")
+BF16_PROBE_SRC = os.path.join(ROOT, "tests", "bf16_mfma_probe.hip")
+BF16_PROBE_LIB = os.path.join(ROOT, "tests", "libbf16_mfma_probe.so")
 
 
 def build_probe() -> str:
-    """Test infrastructure: the probes the GPU tests run (the FP8 matrix instruction's accuracy, and
-    the issue rates of the forward's inner-loop instructions; one of its modes compares the matrix
+    """Test infrastructure: the probes the GPU tests run (the accuracy of the FP8 and of the bf16
+    matrix instruction, and the issue rates of the forward's inner-loop instructions; one of its modes compares the matrix
     accumulators in AGPRs with the VGPRs that every other mode and the library use)."""
     build(out=ISSUE_LIB, src=ISSUE_SRC, mfma_vgpr_form=False)
+    build(out=BF16_PROBE_LIB, src=BF16_PROBE_SRC)
     return build(out=PROBE_LIB, src=PROBE_SRC)
 
 

@@ -1,0 +1,69 @@
+"""The bf16 forward's derived element bound (tests/fwd_bounds.py) on the CPU.
+
+A float64 simulation of the kernel's arithmetic on the same bf16 inputs (fp32 scores, their scaling
+by scale * log2(e) and the max subtracted in fp32, exp2 in fp32, the row sum in fp32, the weights
+rounded to bf16, P V in fp32, O divided by the sum and rounded to bf16, LSE = ln 2 (m + log2 l) in
+fp32) must stay within the bound on every element, while the bound stays well inside the stated
+tolerance: it is the sharper check the GPU tests add.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_tiled_attention_07_amd.inputs import bf16_bits_from_f32, bf16_bits_to_f32, make_qkv
+from fwd_bounds import check_bounds, element_bounds
+from parity import LSE_TOL, O_TOL
+
+
+def simulate(qb, kb, vb, causal, scale):
+    """The kernel's roundings in numpy float32 (not its order of operations)."""
+    q, k, v = (bf16_bits_to_f32(x).astype(np.float32) for x in (qb, kb, vb))
+    T = q.shape[2]
+    c = np.float32(scale * math.log2(math.e))
+    s = np.matmul(q, np.swapaxes(k, -1, -2)) * c                    # fp32 scores, base-2 units
+    if causal:
+        s = np.where(np.tril(np.ones((T, T), dtype=bool)), s, np.float32(-np.inf))
+    m = s.max(axis=-1, keepdims=True)
+    p = np.exp2(s - m).astype(np.float32)
+    l = p.sum(axis=-1, keepdims=True, dtype=np.float32)
+    p16 = bf16_bits_to_f32(bf16_bits_from_f32(p))
+    o = bf16_bits_to_f32(bf16_bits_from_f32(np.matmul(p16, v) / l))
+    lse = (np.float32(math.log(2)) * (m + np.log2(l)))[..., 0]
+    return o.astype(np.float64), lse.astype(np.float64)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("scale_kind,sigma", [("inv_sqrt_d", 1.0), ("inv_sqrt_d", 2.0), ("0.01", 1.0),
+                                              ("1", 0.5), ("1", 2.0)])
+def test_bound_holds_and_is_sharper(d, causal, scale_kind, sigma):
+    scale = {"inv_sqrt_d": 1.0 / math.sqrt(d), "0.01": 0.01, "1": 1.0}[scale_kind]
+    qb, kb, vb = make_qkv(1, 2, 300, d, seed=d + 7 * int(causal) + int(100 * sigma), sigma=sigma)
+    o_ref, lse_ref = oracle.attention_fwd(qb, kb, vb, causal, scale)
+    o_sim, lse_sim = simulate(qb, kb, vb, causal, scale)
+    bounds = element_bounds(qb, kb, vb, causal, scale)
+    ro, rl = check_bounds(o_sim, lse_sim, o_ref, lse_ref, bounds)
+    assert ro <= 1.0 and rl <= 1.0, (ro, rl)
+    # sharper than the stated tolerance where that one is weak, small outputs of unit-variance
+    # values (with sigma 2 the weights' rounding, 2^-8 W with |v| up to 8, is about that size), and
+    # LSE
+    small = np.abs(o_ref) <= 0.1
+    if sigma <= 1.0 and small.any():
+        assert float(np.quantile(bounds[0][small], 0.9)) < O_TOL / 3
+    assert float(np.median(bounds[1])) < LSE_TOL / 2
+
+
+def test_bound_catches_a_dropped_key():
+    # the last key of every non-causal row left out: an error the stated tolerance admits here
+    T = 1000
+    qb, kb, vb = make_qkv(1, 1, T, 64, seed=5)
+    o_ref, lse_ref = oracle.attention_fwd(qb, kb, vb, False, 0.01)
+    q, k, v = (bf16_bits_to_f32(x).astype(np.float64) for x in (qb, kb, vb))
+    s = 0.01 * q[0, 0] @ k[0, 0, :T - 1].T
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    o_bad = ((p @ v[0, 0, :T - 1]) / p.sum(axis=1, keepdims=True))[None, None]
+    assert np.abs(o_bad - o_ref).max() < O_TOL  # the stated bound does not see it
+    ro, _ = check_bounds(o_bad, lse_ref, o_ref, lse_ref, element_bounds(qb, kb, vb, False, 0.01))
+    assert ro > 1.0

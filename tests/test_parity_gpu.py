@@ -17,6 +17,7 @@ import oracle
 import exact_tiled_attention_07_amd as fa
 from exact_tiled_attention_07_amd.inputs import WORKLOADS, bf16_bits_from_f32, bf16_bits_to_f32, make_qkv, to_torch_bf16
 
+from fwd_bounds import check_bounds, element_bounds
 from parity import assert_parity, assert_rms, compare, record
 
 pytestmark = pytest.mark.gpu
@@ -50,7 +51,16 @@ def full_check(qb, kb, vb, causal, scale, label):
     stats = compare(o, lse, o_ref, lse_ref)
     say(f"[gpu] {label} {stats}")
     assert_parity(stats, label)
+    assert_within_derived_bound(o, lse, o_ref, lse_ref, qb, kb, vb, causal, scale, label)
     return o, lse, stats
+
+
+def assert_within_derived_bound(o, lse, o_ref, lse_ref, qb, kb, vb, causal, scale, label):
+    """Every element within the bound derived from the kernel's roundings (tests/fwd_bounds.py),
+    which is sharper than the stated tolerance where |O| is small."""
+    ro, rl = check_bounds(o, lse, o_ref, lse_ref, element_bounds(qb, kb, vb, causal, scale))
+    say(f"[gpu] {label} derived bound: worst |dO| at {ro:.3f} of it, |dLSE| at {rl:.3f}")
+    assert ro <= 1.0 and rl <= 1.0, (label, ro, rl)
 
 
 def sample_rows(B, H, T, n_random, seed):
@@ -231,6 +241,7 @@ def test_ragged_and_tiny_lengths_both_launches(T, causal):
     for bm, bn, w in ((128, 64, 4), (64, 64, 4)):
         o, lse = run_gpu_ex(qb, kb, vb, causal, 0.125, bm, bn, w)
         assert_parity(compare(o, lse, o_ref, lse_ref), f"T={T} tile {bm}x{bn}x{w}")
+        assert_within_derived_bound(o, lse, o_ref, lse_ref, qb, kb, vb, causal, 0.125, f"T={T} tile {bm}x{bn}x{w}")
         if causal:  # row 0 sees key 0 alone: O[0] = V[0] bit for bit, whichever wave holds it
             np.testing.assert_array_equal(o[:, :, 0, :], bf16_bits_to_f32(vb)[:, :, 0, :])
 

@@ -3,7 +3,7 @@ that every run draws the same cases).
 
 Each case draws B, H, T <= 300, d in {64, 128}, causal or not, scale in {1/sqrt(d), 0.01, 1} and an
 input magnitude, runs the default launch on the GPU and compares every element with the oracle at
-the dense tolerance. Small shapes, so the whole file takes seconds; the fixed cases of the other
+the dense tolerance and within the bound derived from the kernel's roundings (tests/fwd_bounds.py). Small shapes, so the whole file takes seconds; the fixed cases of the other
 files cover the large ones.
 """
 import math
@@ -17,6 +17,7 @@ import oracle
 import exact_tiled_attention_07_amd as fa
 from exact_tiled_attention_07_amd.inputs import make_qkv, to_torch_bf16
 
+from fwd_bounds import check_bounds, element_bounds
 from parity import assert_parity, compare
 
 pytestmark = pytest.mark.gpu
@@ -39,5 +40,9 @@ def test_random_shapes_against_oracle(B, H, T, d, causal, scale_kind, sigma, see
     o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.attention_fwd(qb, kb, vb, causal, scale)
-    stats = compare(o.float().cpu().numpy(), lse.cpu().numpy(), o_ref, lse_ref)
-    assert_parity(stats, f"B{B} H{H} T{T} d{d} causal={causal} scale={scale} sigma={sigma}")
+    o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
+    label = f"B{B} H{H} T{T} d{d} causal={causal} scale={scale} sigma={sigma}"
+    assert_parity(compare(o, lse, o_ref, lse_ref), label)
+    # and every element within the bound derived from the kernel's roundings (tests/fwd_bounds.py)
+    ro, rl = check_bounds(o, lse, o_ref, lse_ref, element_bounds(qb, kb, vb, causal, scale))
+    assert ro <= 1.0 and rl <= 1.0, (label, ro, rl)
