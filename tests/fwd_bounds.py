@@ -36,22 +36,31 @@ EPS_BF16_SUM = 2.0 ** -23  # per addition of a recursive fp32 sum (the P V chain
 EPS_BF16_QK = 2.0 ** -22   # per unit of sum_c |q_c k_c|, the score chain over the head dimension
 
 
-def element_bounds(qb, kb, vb, causal, scale):
+def element_bounds(qb, kb, vb, causal, scale, block_mask=None, bm=128, bn=64):
     """(bound on |dO| [B,H,T,d], bound on |dLSE| [B,H,T]) for bf16 inputs (uint16 bits [B,H,T,d]),
-    one head at a time with T x T float64 matrices (for the moderate T of the tests using it)."""
+    one head at a time with T x T float64 matrices (for the moderate T of the tests using it).
+    block_mask (uint8 [1 or B*H, ceil(T/bm), ceil(T/bn)], the block-sparse forward's) hides the
+    blocks it does not set; rows that see no key get an infinite bound (they are checked for
+    exactness on their own)."""
     B, H, T, d = qb.shape
     bo, bl = np.empty((B, H, T, d)), np.empty((B, H, T))
-    hidden = ~np.tril(np.ones((T, T), dtype=bool)) if causal else np.zeros((T, T), dtype=bool)
-    n = np.arange(1, T + 1, dtype=np.float64) if causal else np.full(T, float(T))
-    sums = (n + np.ceil(n / 64) + 2) * 2.0 ** -23
+    causal_hidden = ~np.tril(np.ones((T, T), dtype=bool)) if causal else np.zeros((T, T), dtype=bool)
     for b in range(B):
         for h in range(H):
+            hidden = causal_hidden
+            if block_mask is not None:
+                mh = block_mask[0 if block_mask.shape[0] == 1 else b * H + h].astype(bool)
+                hidden = hidden | ~np.repeat(np.repeat(mh, bm, axis=0), bn, axis=1)[:T, :T]
+            n = (~hidden).sum(axis=1).astype(np.float64)
+            live = n > 0
+            n = np.maximum(n, 1.0)
+            sums = (n + np.ceil(n / 64) + 2) * 2.0 ** -23
             q, k, v = (bf16_bits_to_f32(x[b, h]).astype(np.float64) for x in (qb, kb, vb))
             s = scale * (q @ k.T)
             abs_s = np.abs(s)
             np.putmask(abs_s, hidden, 0.0)
             np.putmask(s, hidden, -np.inf)
-            m = s.max(axis=1)
+            m = np.where(live, s.max(axis=1), 0.0)
             a = np.abs(q) @ np.abs(k).T
             np.putmask(a, hidden, 0.0)
             ds = EPS_BF16_QK * abs(scale) * a.max(axis=1)
@@ -60,7 +69,7 @@ def element_bounds(qb, kb, vb, causal, scale):
             s -= m[:, None]
             p = np.exp(s, out=s)
             np.putmask(p, hidden, 0.0)
-            L = p.sum(axis=1)
+            L = np.where(live, p.sum(axis=1), 1.0)
             p /= L[:, None]
             W = p @ np.abs(v)
             o = p @ v
@@ -69,12 +78,15 @@ def element_bounds(qb, kb, vb, causal, scale):
             rel = (eta + sums + n * EPS_BF16_SUM)[:, None]
             bo[b, h] = 1.01 * (2.0 ** -8 * (np.abs(o) + W) + rel * (W + np.abs(o))) + 1e-7
             bl[b, h] = 1.01 * (ds + da + sums + 2.0 ** -21 * (np.abs(m) + np.log(L) + np.abs(lse))) + 1e-7
+            bo[b, h][~live] = np.inf
+            bl[b, h][~live] = np.inf
     return bo, bl
 
 
 def check_bounds(o_gpu, lse_gpu, o_ref, lse_ref, bounds):
     """Ratios of the errors to the bound: (worst over O, worst over LSE)."""
     bo, bl = bounds
-    ro = np.abs(np.asarray(o_gpu, dtype=np.float64) - o_ref) / bo
-    rl = np.abs(np.asarray(lse_gpu, dtype=np.float64) - lse_ref) / bl
+    fo, fl = np.isfinite(bo), np.isfinite(bl)  # rows that see no key are checked on their own
+    ro = np.abs(np.asarray(o_gpu, dtype=np.float64)[fo] - np.asarray(o_ref)[fo]) / bo[fo]
+    rl = np.abs(np.asarray(lse_gpu, dtype=np.float64)[fl] - np.asarray(lse_ref)[fl]) / bl[fl]
     return float(ro.max(initial=0.0)), float(rl.max(initial=0.0))

@@ -67,3 +67,39 @@ def test_bound_catches_a_dropped_key():
     assert np.abs(o_bad - o_ref).max() < O_TOL  # the stated bound does not see it
     ro, _ = check_bounds(o_bad, lse_ref, o_ref, lse_ref, element_bounds(qb, kb, vb, False, 0.01))
     assert ro > 1.0
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_bound_with_a_block_mask(causal):
+    # the block-sparse form: the bound over the visible blocks holds for the simulation of the same
+    # roundings over those blocks, rows that see nothing get no bound, and an all-ones mask gives
+    # the dense bound
+    T, d = 300, 64
+    qb, kb, vb = make_qkv(1, 2, T, d, seed=61)
+    rng = np.random.default_rng(3)
+    mask = (rng.random((2, 3, 5)) < 0.5).astype(np.uint8)
+    mask[1, 2, :] = 0                                   # head 1: query block 2 sees nothing
+    o_ref, lse_ref = oracle.attention_fwd_blockmask(qb, kb, vb, causal, 0.125, mask, 128, 64)
+    bo, bl = element_bounds(qb, kb, vb, causal, 0.125, block_mask=mask)
+    dead = np.isneginf(lse_ref)
+    assert dead[0, 1, 256:].all() and np.isinf(bl[dead]).all() and np.isfinite(bl[~dead]).all()
+    # the simulation, with the hidden blocks' scores at -inf
+    q, k, v = (bf16_bits_to_f32(x).astype(np.float32) for x in (qb, kb, vb))
+    vis = np.repeat(np.repeat(mask.astype(bool), 128, axis=1), 64, axis=2)[:, :T, :T][None]
+    if causal:
+        vis = vis & np.tril(np.ones((T, T), dtype=bool))
+    c = np.float32(0.125 * math.log2(math.e))
+    s = np.where(vis, np.matmul(q, np.swapaxes(k, -1, -2)) * c, np.float32(-np.inf))
+    m = np.where(vis.any(axis=-1, keepdims=True), s.max(axis=-1, keepdims=True), np.float32(0))
+    p = np.exp2(s - m).astype(np.float32)
+    l = p.sum(axis=-1, keepdims=True, dtype=np.float32)
+    p16 = bf16_bits_to_f32(bf16_bits_from_f32(p))
+    with np.errstate(invalid="ignore", divide="ignore"):
+        o = bf16_bits_to_f32(bf16_bits_from_f32(np.matmul(p16, v) / l)).astype(np.float64)
+        lse = (np.float32(math.log(2)) * (m + np.log2(l)))[..., 0].astype(np.float64)
+    ro, rl = check_bounds(o, lse, o_ref, lse_ref, (bo, bl))
+    assert ro <= 1.0 and rl <= 1.0, (ro, rl)
+    dense = element_bounds(qb, kb, vb, causal, 0.125)
+    full = element_bounds(qb, kb, vb, causal, 0.125, block_mask=np.ones((1, 3, 5), dtype=np.uint8))
+    np.testing.assert_allclose(full[0], dense[0], rtol=1e-12)
+    np.testing.assert_allclose(full[1], dense[1], rtol=1e-12)

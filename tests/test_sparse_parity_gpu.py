@@ -15,6 +15,7 @@ import oracle
 import exact_tiled_attention_07_amd as fa
 from exact_tiled_attention_07_amd.inputs import WORKLOADS, make_qkv, sparse_mask, to_torch_bf16
 
+from fwd_bounds import check_bounds, element_bounds
 from parity import assert_parity, assert_rms, compare
 
 pytestmark = pytest.mark.gpu
@@ -52,6 +53,10 @@ def check(qb, kb, vb, mask, causal, scale, label, rms=False):
     assert_parity(stats, label)
     if rms:  # i.i.d. zero-mean V over many rows: the relative RMS check too
         assert_rms(stats, label)
+    if qb.shape[2] <= 4096:  # and the bound derived from the kernel's roundings (T x T matrices)
+        ro, rl = check_bounds(o, lse, o_ref, lse_ref, element_bounds(qb, kb, vb, causal, scale, block_mask=mask))
+        say(f"[gpu sparse] {label} derived bound: worst |dO| at {ro:.3f} of it, |dLSE| at {rl:.3f}")
+        assert ro <= 1.0 and rl <= 1.0, (label, ro, rl)
     return o, lse
 
 
