@@ -51,6 +51,7 @@ def check_partial(qb, kb, vb, causal, scale, k_begin, k_end, label):
     stats = compare(o[live], lse[live], o_ref[live], lse_ref[live])
     say(f"[gpu splitkv] partial {label} {stats} empty rows {int(empty.sum())}")
     assert_parity(stats, label)
+    assert_rms(stats, label)  # i.i.d. zero-mean V; the stated bound alone is weak where |O| is small
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -210,6 +211,9 @@ def check_against_cross(o, lse, ref, label, sampled=None):
     stats = compare(o[live], lse[live], o_ref[live], lse_ref[live])
     say(f"[gpu splitkv] {label} {stats} empty rows {int(empty.sum())}")
     assert_parity(stats, label)
+    # i.i.d. zero-mean V: a decode row over thousands of keys has |O| ~ 1e-2, where the stated bound
+    # alone would admit an error the size of O
+    assert_rms(stats, label)
 
 
 @pytest.mark.parametrize("causal", [True, False])
