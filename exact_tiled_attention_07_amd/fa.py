@@ -11,6 +11,7 @@ import ctypes
 import math
 import os
 import re
+import threading
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfa.so")
@@ -26,6 +27,7 @@ FA_ERR_TILE = -6
 FA_ERR_SCRATCH = -7
 
 _lib = None
+_lib_lock = threading.Lock()
 
 
 class FaError(RuntimeError):
@@ -54,10 +56,17 @@ class _Int(ctypes.c_int):
 
 
 def lib():
-    """Load libfa.so (once). Raises if it has not been built."""
+    """Load libfa.so (once; safe from several threads). Raises if it has not been built."""
     global _lib
     if _lib is not None:
         return _lib
+    with _lib_lock:
+        if _lib is None:
+            _lib = _load()
+    return _lib
+
+
+def _load():
     if not os.path.exists(LIB_PATH):
         raise FileNotFoundError(
             f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
@@ -89,7 +98,6 @@ def lib():
     L.fa_bwd.restype = ctypes.c_int
     L.fa_strerror.argtypes = [i]
     L.fa_strerror.restype = ctypes.c_char_p
-    _lib = L
     return L
 
 

@@ -25,8 +25,10 @@
  *   - The caller owns every buffer. The library never allocates, frees or keeps a pointer after the
  *     call returns. o and lse must not overlap q, k, v or each other.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the default stream). They return
- *     after enqueueing the kernel and never synchronise. The library keeps no mutable global state
- *     and is safe to call from several host threads.
+ *     after enqueueing the kernel and never synchronise. Apart from the address of
+ *     fa_fwd_splitkv_noalloc's fixed buffer, looked up once per device and kept in an atomic, the
+ *     library keeps no mutable global state; every entry point is safe to call from several host
+ *     threads at once (fa_fwd_splitkv_noalloc's calls that overlap on one GPU share its buffer).
  *   - A call enqueues kernel launches only (no allocation, memset, copy or synchronisation), so it
  *     may be captured into a HIP graph on a capturing stream and replayed.
  *   - Arguments are checked before anything is launched; on any error nothing is written.
