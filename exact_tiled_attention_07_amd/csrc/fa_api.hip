@@ -190,6 +190,12 @@ int resolve_tile(int d, int T, int64_t BH, bool causal, int block_m, int block_n
   return *out ? FA_OK : FA_ERR_TILE;
 }
 
+// The kernels take the scores into exp2 as s * (scale * log2 e) in fp32, so that factor must be a
+// finite positive fp32 number too (scale below about 2.36e38), not only scale itself.
+bool scale_ok(float scale) {
+  return std::isfinite(scale) && scale > 0.0f && std::isfinite(scale * fa::kLog2e);
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return na && nb && x < y + nb && y < x + na;
@@ -200,7 +206,7 @@ int launch(const void* q, const void* k, const void* v, void* o, float* lse, int
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   int rc = check_sizes(B, H, T, d);
   if (rc != FA_OK) return rc;
-  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
   const TileEntry* tile = nullptr;
   rc = resolve_tile(d, T, (int64_t)B * H, causal != 0, block_m, block_n, waves, &tile);
   if (rc != FA_OK) return rc;
@@ -243,7 +249,7 @@ int launch_sparse(const void* q, const void* k, const void* v, void* o, float* l
   if (rc != FA_OK) return rc;
   if (T > FA_SPARSE_MAX_T) return FA_ERR_INVALID_ARG;
   if (mask_heads != 1 && (int64_t)mask_heads != (int64_t)B * H) return FA_ERR_INVALID_ARG;
-  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) return FA_ERR_ALIGNMENT;
   if ((uintptr_t)lse & 3u) return FA_ERR_ALIGNMENT;
   const size_t n_elem = (size_t)B * H * T * d;
@@ -291,7 +297,7 @@ int check_partial_args(const void* q, const void* k, const void* v, const float*
   int rc = check_sizes(B, H, T, d);
   if (rc != FA_OK) return rc;
   if (Tk < 0 || Tk > FA_MAX_T) return FA_ERR_INVALID_ARG;
-  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o_part) & 15u) return FA_ERR_ALIGNMENT;
   if ((uintptr_t)lse_part & 3u) return FA_ERR_ALIGNMENT;
   const size_t rows = (size_t)B * H * T, krows = (size_t)B * H * Tk;
@@ -446,7 +452,7 @@ int launch_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
   int rc = check_sizes(B, H, T, d);
   if (rc != FA_OK) return rc;
   if (Tk < 0 || Tk > FA_MAX_T) return FA_ERR_INVALID_ARG;
-  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
   if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15u) || ((uintptr_t)lse & 3u))
     return FA_ERR_ALIGNMENT;
   if ((size_t)B * H * T == 0) return FA_OK;  // an empty problem: nothing launched, no scratch used
@@ -509,7 +515,7 @@ int launch_bwd(const void* q, const void* k, const void* v, const void* o, const
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !delta) return FA_ERR_NULL;
   int rc = check_sizes(B, H, T, d);
   if (rc != FA_OK) return rc;
-  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o | (uintptr_t)dout |
        (uintptr_t)dq | (uintptr_t)dk | (uintptr_t)dv) & 15u)
     return FA_ERR_ALIGNMENT;

@@ -33,7 +33,8 @@
  *     may be captured into a HIP graph on a capturing stream and replayed.
  *   - Arguments are checked before anything is launched; on any error nothing is written.
  *   - B*H*T == 0 is a valid empty problem: FA_OK, nothing launched, nothing written.
- *   - Inputs must be finite. NaN or Inf inputs give unspecified outputs (no error is raised).
+ *   - Inputs must be finite. NaN or Inf inputs give unspecified outputs (no error is raised), and so
+ *     do scaled scores (scale * q.k) beyond fp32's range, which no check can see before launching.
  */
 #ifndef FA_H_
 #define FA_H_
@@ -47,7 +48,8 @@ extern "C" {
 typedef enum fa_status {
   FA_OK = 0,
   FA_ERR_NULL = -1,           /* a required pointer is NULL */
-  FA_ERR_INVALID_ARG = -2,    /* negative size, size too large, scale not finite and > 0, overlap */
+  FA_ERR_INVALID_ARG = -2,    /* negative size, size too large, scale not finite and > 0 (or
+                                 scale * log2 e not finite), overlap */
   FA_ERR_UNSUPPORTED_D = -3,  /* head dim d is not 64 or 128 */
   FA_ERR_ALIGNMENT = -4,      /* q, k, v or o not 16-byte aligned, or lse not 4-byte aligned */
   FA_ERR_HIP = -5,            /* the kernel launch itself failed (its own status, not an earlier
@@ -71,7 +73,8 @@ typedef enum fa_status {
  *            T <= FA_MAX_T, B*H <= FA_MAX_BH
  *   d        head dimension: 64 or 128
  *   causal   nonzero: query i sees keys 0..i (the causal mask); zero: it sees all T keys
- *   scale    finite and > 0; the scores are scale * q.k (1/sqrt(d) for standard attention)
+ *   scale    finite and > 0, and scale * log2(e) finite in fp32 (scale below about 2.36e38); the
+ *            scores are scale * q.k (1/sqrt(d) for standard attention)
  *   stream   hipStream_t to launch on (NULL: default stream)
  * The launch depends on the sizes (fa_fwd_plan reports it): 128 queries x 64 keys per workgroup and
  * tile, or, at d = 64 for short sequences, one of two others. With nq = ceil(T/128) query blocks

@@ -60,8 +60,9 @@ def test_unsupported_head_dim(d):
     assert call(d=d) == fa.FA_ERR_UNSUPPORTED_D
 
 
-@pytest.mark.parametrize("scale", [0.0, -0.125, float("inf"), float("nan")])
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("inf"), float("nan"), 3.0e38])
 def test_bad_scale(scale):
+    # 3e38 is a finite fp32 whose product with log2(e), the factor the kernels use, is not
     assert call(scale=scale) == fa.FA_ERR_INVALID_ARG
 
 
@@ -229,7 +230,7 @@ def test_bwd_sizes_head_dim_scale():
     assert call_bwd(B=1 << 13, H=1 << 12) == fa.FA_ERR_INVALID_ARG
     assert call_bwd(d=96) == fa.FA_ERR_UNSUPPORTED_D  # the backward takes d = 64 or 128
     assert call_bwd(d=32) == fa.FA_ERR_UNSUPPORTED_D
-    for sc in (0.0, -1.0, float("nan"), float("inf")):
+    for sc in (0.0, -1.0, float("nan"), float("inf"), 3.0e38):
         assert call_bwd(scale=sc) == fa.FA_ERR_INVALID_ARG
 
 
@@ -271,6 +272,7 @@ def test_sparse_checks():
     assert call_sparse(mask_heads=2) == fa.FA_ERR_INVALID_ARG  # neither 1 nor B*H
     assert call_sparse(B=2, H=3, mask_heads=6, T=0) == fa.FA_OK
     assert call_sparse(scale=0.0) == fa.FA_ERR_INVALID_ARG
+    assert call_sparse(scale=3.0e38) == fa.FA_ERR_INVALID_ARG
     assert call_sparse(q=A + 8) == fa.FA_ERR_ALIGNMENT
     assert call_sparse(o=6 * A) == fa.FA_ERR_INVALID_ARG      # output over the mask
     assert call_sparse(T=0) == fa.FA_OK and call_sparse(T=0, d=128, causal=0) == fa.FA_OK
@@ -299,6 +301,8 @@ def test_partial_checks():
     assert call_partial(T=4, Tk=-1, k_end=0) == fa.FA_ERR_INVALID_ARG
     assert call_partial(T=4, Tk=100, k_end=200) == fa.FA_ERR_INVALID_ARG  # range past Tk
     assert call_partial(T=0, Tk=100, k_end=100) == fa.FA_OK         # no query: nothing launched
+    for sc in (0.0, float("inf"), 3.0e38):                          # 3e38 * log2(e) overflows fp32
+        assert call_partial(scale=sc) == fa.FA_ERR_INVALID_ARG
 
 
 def call_splitkv(B=1, H=2, T=4, Tk=1000, d=64, n=4, ws=16 * A, ws_bytes=None, **kw):
@@ -408,6 +412,7 @@ def test_splitkv_noalloc_checks():
     assert call_noalloc(d=96) == fa.FA_ERR_UNSUPPORTED_D
     assert call_noalloc(scale=0.0) == fa.FA_ERR_INVALID_ARG
     assert call_noalloc(scale=float("nan")) == fa.FA_ERR_INVALID_ARG
+    assert call_noalloc(scale=3.0e38) == fa.FA_ERR_INVALID_ARG
     assert call_noalloc(q=A + 8) == fa.FA_ERR_ALIGNMENT
     assert call_noalloc(lse=5 * A + 2) == fa.FA_ERR_ALIGNMENT
     # an empty problem is a no-op
