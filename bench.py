@@ -547,7 +547,10 @@ def parity_check(wl, o, lse, ref, n_heads):
             "max_err_o": st["max_err_o"], "max_err_lse": st["max_err_lse"],
             "n_ulp_clause": st["n_ulp_clause"], "n_fail": st["n_fail_o"] + st["n_fail_lse"] + st["n_nonfinite"],
             "pass": passed(st),
-            "tolerance": "|dO| <= 1.5e-2, or one bf16 ulp where |O_ref| >= 2; |dLSE| <= 1e-3"}
+            "tolerance": "|dO| <= 1.5e-2, or one bf16 ulp where |O_ref| >= 2; |dLSE| <= 1e-3",
+            # relative RMS error of O: two bf16 roundings (P, then O) give at most 2^-7 / sqrt(12)
+            # = 2.26e-3 for i.i.d. zero-mean V; the tests allow twice that
+            "rms_rel_err_o": st["rms_err_o"] / st["rms_ref_o"] if st["rms_ref_o"] > 0 else 0.0}
 
 
 def copy_calibration(mib):

@@ -86,6 +86,8 @@ def test_bench_parity_check_uses_the_oracle_output_and_catches_errors():
     p = bench.parity_check(wl, o, lse, ref, n_heads)
     assert p["pass"] and p["n_fail"] == 0 and p["rows"] == wl.B * wl.H * wl.T
     assert p["max_err_o"] <= 2.0 ** -7  # only the bf16 rounding of the oracle's own output (|O| < 4)
+    # that one rounding: relative RMS about 2^-7 / sqrt(24)
+    assert 0.5 * 2.0 ** -7 / 24 ** 0.5 < p["rms_rel_err_o"] < 1.5 * 2.0 ** -7 / 24 ** 0.5
     o[0, 1, 17, 5] += 0.05  # one element off by more than the tolerance
     lse[0, 0, 3] += 2e-3
     p = bench.parity_check(wl, o, lse, ref, n_heads)
