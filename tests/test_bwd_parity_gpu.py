@@ -35,17 +35,21 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 # |gpu - ref| <= ELEM_TOL * (|ref| + rms of the reference over its head), and rms(gpu - ref) <=
 # RMS_TOL * rms(ref) per tensor: twice the rounding model's worst figures (tests/bwd_tolerance.py)
-from bwd_tolerance import ELEM_TOL, RMS_TOL  # noqa: E402
+from bwd_tolerance import ELEM_TOL, RMS_TOL, o_rounding_allowance  # noqa: E402
 
 
 def say(msg):
     print(msg, flush=True)
 
 
-def grad_tolerance(name, gpu, ref, atol=0.0):
+def grad_tolerance(name, gpu, ref, atol=0.0, allowance=None):
     """Element and RMS check of one gradient tensor [B, H, T, d] (or delta [B, H, T]); atol is the
-    absolute floor of the fp32 cancellation in dS (see the module docstring)."""
+    absolute floor of the fp32 cancellation in dS (see the module docstring). Where the relative
+    bounds fail, `allowance()` (dQ and dK only) gives the per-element bound on what the forward's
+    rounded O does through D (bwd_tolerance.o_rounding_allowance), admitted with a 10% margin."""
     stats = grad_stats(gpu, ref, atol)
+    if allowance is not None and (stats["max_ratio"] > ELEM_TOL or stats["rms_ratio"] > RMS_TOL):
+        stats = dict(grad_stats(gpu, ref, atol + 1.1 * allowance()), o_rounding_allowance=True)
     assert stats["nonfinite"] == 0, (name, stats)
     assert stats["max_ratio"] <= ELEM_TOL, (name, stats)
     assert stats["rms_ratio"] <= RMS_TOL, (name, stats)
@@ -66,20 +70,35 @@ def cancellation_floors(qb, kb, vb, dob, causal, scale, i):
             2 * scale * float(q.max(initial=0.0)) * cancel * one_key_k[..., None], 0.0, 0.0)
 
 
-def run_gpu(qb, kb, vb, dob, causal, scale):
+def run_gpu(qb, kb, vb, dob, causal, scale, with_o=False):
     q, k, v, do = (to_torch_bf16(x, DEV) for x in (qb, kb, vb, dob))
     o, lse = fa.fwd(q, k, v, causal=causal, scale=scale)
     dq, dk, dv, delta = fa.bwd(q, k, v, o, lse, do, causal=causal, scale=scale)
     torch.cuda.synchronize()
-    return [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv, delta)]
+    out = [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv, delta)]
+    return (out, o.float().cpu().numpy().astype(np.float64)) if with_o else out
+
+
+def allowances(qb, kb, vb, dob, causal, scale, o_used):
+    """Lazy per-tensor allowance callables for grad_tolerance (computed at most once)."""
+    memo = []
+
+    def get(i):
+        if not memo:
+            memo.extend(o_rounding_allowance(qb, kb, vb, dob, causal, scale, o_used))
+        return memo[i]
+
+    return (lambda: get(0), lambda: get(1), None, None)
 
 
 def check(qb, kb, vb, dob, causal, scale, label, keep=False):
     say(f"[gpu bwd] {label} shape={qb.shape} causal={causal} scale={scale}")
-    got = run_gpu(qb, kb, vb, dob, causal, scale)
+    got, o_gpu = run_gpu(qb, kb, vb, dob, causal, scale, with_o=True)
     ref = oracle.attention_bwd(qb, kb, vb, dob, causal, scale)
     floors = cancellation_floors(qb, kb, vb, dob, causal, scale, np.arange(qb.shape[2]).reshape(1, 1, -1))
-    stats = {n: grad_tolerance(n, g, r, a) for n, g, r, a in zip(("dq", "dk", "dv", "delta"), got, ref, floors)}
+    extra = allowances(qb, kb, vb, dob, causal, scale, o_gpu)
+    stats = {n: grad_tolerance(n, g, r, a, x)
+             for n, g, r, a, x in zip(("dq", "dk", "dv", "delta"), got, ref, floors, extra)}
     say(f"[gpu bwd] {label} " + " ".join(f"{n}: {s['max_ratio']:.4f}/{s['rms_ratio']:.4f}"
                                          for n, s in stats.items()))
     if keep:
@@ -146,6 +165,19 @@ def test_bwd_d128_workload_first_heads():
     say(f"[gpu bwd] {label} " + " ".join(f"{n}: {s['max_ratio']:.4f}/{s['rms_ratio']:.4f}"
                                          for n, s in stats.items()))
     record_bwd(label, stats)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("T", [2, 3, 17])
+def test_bwd_heads_dominated_by_one_key(T, d, causal):
+    # short heads at scale 1: every row's weights are dominated by one key, dQ and dK are near zero
+    # and their error is the forward's rounded O seen through D; the relative bounds alone fail
+    # here, and the allowance for that rounding (bwd_tolerance.o_rounding_allowance) must cover it.
+    # (B1 H1 T2 d64, non-causal, inputs of seeds 0 and 1 is the case a randomised run found.)
+    qb, kb, vb = make_qkv(1, 1, T, d, seed=0)
+    dob, _, _ = make_qkv(1, 1, T, d, seed=1)
+    check(qb, kb, vb, dob, causal, 1.0, f"one-key-dominated T={T} d={d}")
 
 
 def test_bwd_long_sequence():

@@ -47,3 +47,39 @@ def test_model_without_roundings_is_the_oracle():
     for g, r in zip(got[:3], ref[:3]):
         # only the fp32 LSE remains: relative error ~1e-7
         np.testing.assert_allclose(g, r, rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_o_rounding_allowance_covers_a_head_dominated_by_one_key(causal):
+    # two tokens at scale 1: every row's weights are dominated by one key, dS is a small difference
+    # of two large terms everywhere, and dQ, dK are near zero. The rounding model (bf16 O in D, bf16
+    # P and dS) then fails the relative bounds, and its excess is what bwd_tolerance's allowance,
+    # computed from the same bf16 O, bounds
+    from bwd_tolerance import o_rounding_allowance
+    from exact_tiled_attention_07_amd.inputs import make_qkv
+
+    qb, kb, vb = make_qkv(1, 1, 2, 64, seed=0)
+    dob, _, _ = make_qkv(1, 1, 2, 64, seed=1)
+    ref = oracle.attention_bwd(qb, kb, vb, dob, causal, 1.0)
+    got = model.model_bwd(qb, kb, vb, dob, causal, 1.0)
+    o16 = model.bf16(oracle.attention_fwd(qb, kb, vb, causal, 1.0)[0])
+    aq, ak = o_rounding_allowance(qb, kb, vb, dob, causal, 1.0, o16)
+    plain = [model.grad_stats(g, r) for g, r in zip(got[:2], ref[:2])]
+    if not causal:  # (causal: row 0 sees one key, row 1 two; whichever way, the allowance must cover)
+        assert any(s["max_ratio"] > ELEM_TOL or s["rms_ratio"] > RMS_TOL for s in plain)
+    for g, r, a in zip(got[:2], ref[:2], (aq, ak)):
+        s = model.grad_stats(g, r, 1.1 * a)
+        assert s["max_ratio"] <= ELEM_TOL and s["rms_ratio"] <= RMS_TOL, s
+
+
+def test_o_rounding_allowance_is_small_in_an_ordinary_head():
+    # in a head of the tests' usual scale the allowance is a small part of the gradients: it only
+    # matters where the relative bounds cannot work
+    from bwd_tolerance import o_rounding_allowance
+
+    qb, kb, vb, dob = model.inputs(1, 2, 300, 13)
+    ref = oracle.attention_bwd(qb, kb, vb, dob, True, 0.125)
+    o16 = model.bf16(oracle.attention_fwd(qb, kb, vb, True, 0.125)[0])
+    aq, ak = o_rounding_allowance(qb, kb, vb, dob, True, 0.125, o16)
+    assert np.sqrt((aq ** 2).mean()) < 0.02 * np.sqrt((ref[0] ** 2).mean())
+    assert np.sqrt((ak ** 2).mean()) < 0.02 * np.sqrt((ref[1] ** 2).mean())
