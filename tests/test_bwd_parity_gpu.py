@@ -180,6 +180,16 @@ def test_bwd_heads_dominated_by_one_key(T, d, causal):
     check(qb, kb, vb, dob, causal, 1.0, f"one-key-dominated T={T} d={d}")
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("sigma,scale,vmul", [(8.0, 3.0, 1.0), (4.0, 1.0, 100.0), (1.0, 0.125, 0.01)])
+def test_bwd_extreme_magnitudes(sigma, scale, vmul, causal):
+    # scores in the thousands, V times 100 or times 0.01: the backward's tolerance is relative to
+    # each head's own scale (plus the allowance for heads dominated by one key), so it holds here too
+    qb, kb, vb, dob = inputs(1, 2, 257, 95, sigma=sigma)
+    vb = bf16_bits_from_f32((bf16_bits_to_f32(vb) * np.float32(vmul)).astype(np.float32))
+    check(qb, kb, vb, dob, causal, scale, f"extreme sigma={sigma} scale={scale} V x{vmul}")
+
+
 def test_bwd_long_sequence():
     # one twelfth of the T = 4096 workload (4 of its 48 heads), inputs at its sigma of 2
     check(*inputs(1, 4, 4096, 4, sigma=2.0), True, 0.125, "T=4096 sigma2 (4 heads)")
