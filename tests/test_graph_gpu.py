@@ -152,3 +152,47 @@ def test_fp8_graph_replays():
         torch.cuda.synchronize()
         assert_same(o, o_e, f"o, replay {r}")
         assert_same(lse, lse_e, f"lse, replay {r}")
+
+
+def test_sparse_partial_merge_noalloc_graph_replays():
+    # the remaining entry points in one graph: the block-sparse forward, two partials and their
+    # merge (into static fp32 part buffers), and the no-alloc split-KV call
+    from exact_tiled_attention_07_amd.inputs import sparse_mask
+
+    B, H, T, d = 1, 3, 700, 64
+    q, k, v = (torch.empty(B, H, T, d, dtype=torch.bfloat16, device=DEV) for _ in range(3))
+    qn = torch.empty(B, H, 5, d, dtype=torch.bfloat16, device=DEV)
+    mask = torch.from_numpy(sparse_mask(T, 0.4, 3)).to(DEV)
+    o_s, o_m, o_n = (torch.empty(B, H, t, d, dtype=torch.bfloat16, device=DEV) for t in (T, T, 5))
+    l_s, l_m, l_n = (torch.empty(B, H, t, dtype=torch.float32, device=DEV) for t in (T, T, 5))
+    op = torch.empty(2, B, H, T, d, dtype=torch.float32, device=DEV)
+    lp = torch.empty(2, B, H, T, dtype=torch.float32, device=DEV)
+
+    def refill(seed):
+        fill((q, k, v), B, H, T, d, seed)
+        qn.copy_(to_torch_bf16(make_qkv(B, H, 5, d, seed=seed + 1)[0], DEV))
+
+    def calls():
+        fa.fwd_sparse(q, k, v, mask, causal=True, out=o_s, lse=l_s)
+        for i, (a, b) in enumerate(((0, 320), (320, T))):
+            fa.fwd_partial(q, k, v, a, b, causal=True, o_part=op[i], lse_part=lp[i])
+        fa.merge(op, lp, out=o_m, lse=l_m)
+        fa.fwd_splitkv_noalloc(qn, k, v, causal=True, n_splits=6, out=o_n, lse=l_n)
+
+    refill(11)
+    g = capture(calls)
+    for r in range(REPLAYS):
+        refill(1100 + r)
+        for t in (o_s, o_m, o_n):
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        e_s = fa.fwd_sparse(q, k, v, mask, causal=True)
+        parts = [fa.fwd_partial(q, k, v, a, b, causal=True) for a, b in ((0, 320), (320, T))]
+        e_m = fa.merge(torch.stack([p[0] for p in parts]), torch.stack([p[1] for p in parts]))
+        e_n = fa.fwd_splitkv(qn, k, v, causal=True, n_splits=6)
+        torch.cuda.synchronize()
+        for (got_o, got_l), (want_o, want_l), name in (((o_s, l_s), e_s, "sparse"), ((o_m, l_m), e_m, "merge"),
+                                                         ((o_n, l_n), e_n, "noalloc splitkv")):
+            assert_same(got_o, want_o, f"{name} o, replay {r}")
+            assert_same(got_l, want_l, f"{name} lse, replay {r}")
