@@ -8,6 +8,12 @@
  *       IN holds q, k, v as bf16 bit patterns ([B,H,T,d] each, in that order). The program copies
  *       them to device memory, runs fa_fwd on a stream of its own, and writes o (bf16 bits) then
  *       lse (fp32) to OUT.
+ *   c_consumer bwd IN OUT B H T d causal scale
+ *       IN holds q, k, v and dO (bf16 bits, [B,H,T,d] each). The program runs fa_fwd, then fa_bwd
+ *       on its outputs, and writes dq, dk, dv (bf16 bits) then delta (fp32) to OUT.
+ *   c_consumer splitkv IN OUT B H T Tk d causal scale n_splits
+ *       IN holds q ([B,H,T,d]) then k and v ([B,H,Tk,d]). The program allocates the workspace that
+ *       fa_splitkv_workspace_bytes asks for, runs fa_fwd_splitkv and writes o then lse to OUT.
  * Exit status 0 on success; anything else prints what failed.
  */
 #include <stdint.h>
@@ -170,10 +176,130 @@ static int forward(int argc, char** argv) {
   return 0;
 }
 
+/* n_in bf16 tensors of the given element counts from path, each copied to a new device buffer */
+static void read_to_device(const char* path, int n_in, const size_t* counts, void** dev) {
+  FILE* f = fopen(path, "rb");
+  int i;
+  CHECK(f != NULL, "cannot open %s", path);
+  for (i = 0; i < n_in; ++i) {
+    const size_t bytes = counts[i] * sizeof(uint16_t);
+    void* host = malloc(bytes);
+    CHECK(host != NULL, "out of host memory");
+    CHECK(fread(host, 1, bytes, f) == bytes, "%s is shorter than its inputs", path);
+    HIP(hipMalloc(&dev[i], bytes));
+    HIP(hipMemcpy(dev[i], host, bytes, hipMemcpyHostToDevice));
+    free(host);
+  }
+  fclose(f);
+}
+
+/* n_out device buffers of the given byte counts, in order, to path */
+static void write_from_device(const char* path, int n_out, void* const* dev, const size_t* bytes) {
+  FILE* f = fopen(path, "wb");
+  int i;
+  CHECK(f != NULL, "cannot open %s", path);
+  for (i = 0; i < n_out; ++i) {
+    void* host = malloc(bytes[i]);
+    CHECK(host != NULL, "out of host memory");
+    HIP(hipMemcpy(host, dev[i], bytes[i], hipMemcpyDeviceToHost));
+    CHECK(fwrite(host, 1, bytes[i], f) == bytes[i], "short write to %s", path);
+    free(host);
+  }
+  CHECK(fclose(f) == 0, "cannot close %s", path);
+}
+
+static int backward(int argc, char** argv) {
+  int B, H, T, d, causal, rc, i;
+  float scale;
+  size_t n, counts[4], out_bytes[4];
+  void *in[4], *o, *out[4];
+  float* lse;
+  hipStream_t stream;
+
+  CHECK(argc == 10, "usage: c_consumer bwd IN OUT B H T d causal scale");
+  B = atoi(argv[4]);
+  H = atoi(argv[5]);
+  T = atoi(argv[6]);
+  d = atoi(argv[7]);
+  causal = atoi(argv[8]);
+  scale = (float)atof(argv[9]);
+  CHECK(B > 0 && H > 0 && T > 0 && d > 0, "sizes must be positive");
+  n = (size_t)B * H * T * d;
+  for (i = 0; i < 4; ++i) counts[i] = n;
+  read_to_device(argv[2], 4, counts, in);  /* q, k, v, dO */
+  HIP(hipMalloc(&o, n * 2));
+  HIP(hipMalloc((void**)&lse, (size_t)B * H * T * 4));
+  for (i = 0; i < 3; ++i) {
+    out_bytes[i] = n * 2;
+    HIP(hipMalloc(&out[i], out_bytes[i]));
+  }
+  out_bytes[3] = (size_t)B * H * T * 4;
+  HIP(hipMalloc(&out[3], out_bytes[3]));
+  HIP(hipStreamCreate(&stream));
+  rc = fa_fwd(in[0], in[1], in[2], o, lse, B, H, T, d, causal, scale, (void*)stream);
+  CHECK(rc == FA_OK, "fa_fwd returned %d (%s)", rc, fa_strerror(rc));
+  rc = fa_bwd(in[0], in[1], in[2], o, lse, in[3], out[0], out[1], out[2], (float*)out[3], B, H, T, d,
+              causal, scale, (void*)stream);
+  CHECK(rc == FA_OK, "fa_bwd returned %d (%s)", rc, fa_strerror(rc));
+  HIP(hipStreamSynchronize(stream));
+  write_from_device(argv[3], 4, out, out_bytes);
+  HIP(hipStreamDestroy(stream));
+  for (i = 0; i < 4; ++i) {
+    HIP(hipFree(in[i]));
+    HIP(hipFree(out[i]));
+  }
+  HIP(hipFree(o));
+  HIP(hipFree(lse));
+  printf("ok\n");
+  return 0;
+}
+
+static int splitkv(int argc, char** argv) {
+  int B, H, T, Tk, d, causal, n_splits, rc, i;
+  float scale;
+  size_t counts[3], out_bytes[2], ws_bytes;
+  void *in[3], *out[2], *ws;
+  hipStream_t stream;
+
+  CHECK(argc == 12, "usage: c_consumer splitkv IN OUT B H T Tk d causal scale n_splits");
+  B = atoi(argv[4]);
+  H = atoi(argv[5]);
+  T = atoi(argv[6]);
+  Tk = atoi(argv[7]);
+  d = atoi(argv[8]);
+  causal = atoi(argv[9]);
+  scale = (float)atof(argv[10]);
+  n_splits = atoi(argv[11]);
+  CHECK(B > 0 && H > 0 && T > 0 && Tk > 0 && d > 0 && n_splits > 0, "sizes must be positive");
+  counts[0] = (size_t)B * H * T * d;
+  counts[1] = counts[2] = (size_t)B * H * Tk * d;
+  read_to_device(argv[2], 3, counts, in);  /* q, k, v */
+  out_bytes[0] = counts[0] * 2;
+  out_bytes[1] = (size_t)B * H * T * 4;
+  for (i = 0; i < 2; ++i) HIP(hipMalloc(&out[i], out_bytes[i]));
+  ws_bytes = fa_splitkv_workspace_bytes(B, H, T, d, n_splits);
+  CHECK(ws_bytes > 0, "fa_splitkv_workspace_bytes returned 0");
+  HIP(hipMalloc(&ws, ws_bytes));
+  HIP(hipStreamCreate(&stream));
+  rc = fa_fwd_splitkv(in[0], in[1], in[2], out[0], (float*)out[1], B, H, T, Tk, d, causal, scale,
+                      n_splits, ws, ws_bytes, (void*)stream);
+  CHECK(rc == FA_OK, "fa_fwd_splitkv returned %d (%s)", rc, fa_strerror(rc));
+  HIP(hipStreamSynchronize(stream));
+  write_from_device(argv[3], 2, out, out_bytes);
+  HIP(hipStreamDestroy(stream));
+  for (i = 0; i < 3; ++i) HIP(hipFree(in[i]));
+  for (i = 0; i < 2; ++i) HIP(hipFree(out[i]));
+  HIP(hipFree(ws));
+  printf("ok\n");
+  return 0;
+}
+
 int main(int argc, char** argv) {
-  CHECK(argc >= 2, "usage: c_consumer host | fwd IN OUT B H T d causal scale");
+  CHECK(argc >= 2, "usage: c_consumer host | fwd ... | bwd ... | splitkv ... (see the file's header)");
   if (strcmp(argv[1], "host") == 0) return host_checks();
   if (strcmp(argv[1], "fwd") == 0) return forward(argc, argv);
+  if (strcmp(argv[1], "bwd") == 0) return backward(argc, argv);
+  if (strcmp(argv[1], "splitkv") == 0) return splitkv(argc, argv);
   CHECK(0, "unknown mode %s", argv[1]);
   return 2;
 }

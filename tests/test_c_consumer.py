@@ -1,5 +1,6 @@
 """libfa.so used from plain C (tests/c_consumer.c): the header compiles as strict C99, the library links
-into a C program, and that program's fa_fwd result agrees with the oracle.
+into a C program, and that program's fa_fwd, fa_bwd and fa_fwd_splitkv results agree with the
+oracle.
 
 The C program is compiled with gcc into pytest's temporary directory (a fraction of a second); it
 runs as a child process, which allocates its own device memory through the HIP runtime's C API.
@@ -15,7 +16,7 @@ import oracle
 from exact_tiled_attention_07_amd import fa
 from exact_tiled_attention_07_amd.inputs import bf16_bits_to_f32, make_qkv
 
-from parity import assert_parity, compare
+from parity import assert_parity, assert_rms, compare
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -80,3 +81,61 @@ def test_c_program_forward_matches_oracle(consumer, tmp_path, B, H, T, d, causal
     stats = compare(o, lse, o_ref, lse_ref)
     print(f"[gpu] c_consumer {stats}", flush=True)
     assert_parity(stats, "c_consumer")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("B,H,T,d,causal", [(1, 2, 300, 64, True), (2, 1, 129, 128, False)])
+def test_c_program_backward_matches_oracle(consumer, tmp_path, B, H, T, d, causal):
+    # fa_fwd then fa_bwd from C, on buffers the program allocates; the backward's tolerance
+    from bwd_tolerance import ELEM_TOL, RMS_TOL
+    from bwd_rounding_model import grad_stats
+
+    qb, kb, vb = make_qkv(B, H, T, d, seed=61 + T)
+    dob, _, _ = make_qkv(B, H, T, d, seed=62 + T)
+    scale = float(np.float32(d ** -0.5))
+    inp, out = tmp_path / "in.bin", tmp_path / "out.bin"
+    with open(inp, "wb") as f:
+        for x in (qb, kb, vb, dob):
+            f.write(np.ascontiguousarray(x, dtype=np.uint16).tobytes())
+    print(f"[gpu] c_consumer bwd B{B} H{H} T{T} d{d} causal={causal}", flush=True)
+    r = subprocess.run([consumer, "bwd", str(inp), str(out), str(B), str(H), str(T), str(d),
+                        str(int(causal)), repr(scale)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    raw = out.read_bytes()
+    n = B * H * T * d
+    assert len(raw) == 3 * 2 * n + 4 * B * H * T
+    got = [bf16_bits_to_f32(np.frombuffer(raw[2 * n * i:2 * n * (i + 1)], dtype=np.uint16)).astype(np.float64)
+           .reshape(B, H, T, d) for i in range(3)]
+    got.append(np.frombuffer(raw[6 * n:], dtype=np.float32).astype(np.float64).reshape(B, H, T))
+    ref = oracle.attention_bwd(qb, kb, vb, dob, causal, scale)
+    for name, g, rf in zip(("dq", "dk", "dv", "delta"), got, ref):
+        st = grad_stats(g, rf)
+        print(f"[gpu] c_consumer bwd {name} {st['max_ratio']:.4f}/{st['rms_ratio']:.4f}", flush=True)
+        assert st["nonfinite"] == 0 and st["max_ratio"] <= ELEM_TOL and st["rms_ratio"] <= RMS_TOL, (name, st)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("B,H,T,Tk,d,causal,n", [(2, 3, 1, 5000, 64, True, 8), (1, 2, 16, 3000, 128, False, 5)])
+def test_c_program_splitkv_matches_oracle(consumer, tmp_path, B, H, T, Tk, d, causal, n):
+    # fa_fwd_splitkv from C with a workspace the program allocates itself
+    qb, _, _ = make_qkv(B, H, T, d, seed=71 + T)
+    _, kb, vb = make_qkv(B, H, Tk, d, seed=72 + Tk)
+    scale = float(np.float32(d ** -0.5))
+    inp, out = tmp_path / "in.bin", tmp_path / "out.bin"
+    with open(inp, "wb") as f:
+        for x in (qb, kb, vb):
+            f.write(np.ascontiguousarray(x, dtype=np.uint16).tobytes())
+    print(f"[gpu] c_consumer splitkv B{B} H{H} T{T} Tk{Tk} d{d} causal={causal} n={n}", flush=True)
+    r = subprocess.run([consumer, "splitkv", str(inp), str(out), str(B), str(H), str(T), str(Tk), str(d),
+                        str(int(causal)), repr(scale), str(n)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stdout + r.stderr
+    raw = out.read_bytes()
+    m = B * H * T * d
+    assert len(raw) == 2 * m + 4 * B * H * T
+    o = bf16_bits_to_f32(np.frombuffer(raw[:2 * m], dtype=np.uint16).reshape(B, H, T, d))
+    lse = np.frombuffer(raw[2 * m:], dtype=np.float32).reshape(B, H, T)
+    o_ref, lse_ref = oracle.attention_fwd_cross(qb, kb, vb, causal, scale)
+    stats = compare(o, lse, o_ref, lse_ref)
+    print(f"[gpu] c_consumer splitkv {stats}", flush=True)
+    assert_parity(stats, "c_consumer splitkv")
+    assert_rms(stats, "c_consumer splitkv")  # decode rows: |O| ~ 2e-2, below the stated bound
