@@ -15,7 +15,9 @@ checks also admit an absolute floor. That happens on the rows with one visible k
 with P = 1 and dP = D): dQ's row 0 of a causal head, and every row of a one-token head (dK's too).
 dP and D are fp32 sums of d products, each off by at most d 2^-24 sum_c |dO_c| max|v|, and the rows
 of P sum to one, so dQ = scale dS K (dK = scale dS^T Q) is off by at most 2 scale d 2^-24 max|k|
-(max|q|) times that. Every other element is held to the relative bounds alone.
+(max|q|) times that. Every other element is held to the relative bounds alone. Every element
+also has the floor 2^-126, the smallest normal fp32 (and bf16) number: an exact gradient below it
+(a weight of exp(-300) times a small difference) cannot be represented by fp32 arithmetic at all.
 """
 import math
 
@@ -37,6 +39,8 @@ DEV = "cuda:0"
 # RMS_TOL * rms(ref) per tensor: twice the rounding model's worst figures (tests/bwd_tolerance.py)
 from bwd_tolerance import ELEM_TOL, RMS_TOL, o_rounding_allowance  # noqa: E402
 
+FP32_MIN_NORMAL = 2.0 ** -126  # below it an exact gradient is not representable in fp32 or bf16
+
 
 def say(msg):
     print(msg, flush=True)
@@ -47,6 +51,7 @@ def grad_tolerance(name, gpu, ref, atol=0.0, allowance=None):
     absolute floor of the fp32 cancellation in dS (see the module docstring). Where the relative
     bounds fail, `allowance()` (dQ and dK only) gives the per-element bound on what the forward's
     rounded O does through D (bwd_tolerance.o_rounding_allowance), admitted with a 10% margin."""
+    atol = atol + FP32_MIN_NORMAL
     stats = grad_stats(gpu, ref, atol)
     if allowance is not None and (stats["max_ratio"] > ELEM_TOL or stats["rms_ratio"] > RMS_TOL):
         stats = dict(grad_stats(gpu, ref, atol + 1.1 * allowance()), o_rounding_allowance=True)
@@ -188,6 +193,18 @@ def test_bwd_extreme_magnitudes(sigma, scale, vmul, causal):
     qb, kb, vb, dob = inputs(1, 2, 257, 95, sigma=sigma)
     vb = bf16_bits_from_f32((bf16_bits_to_f32(vb) * np.float32(vmul)).astype(np.float32))
     check(qb, kb, vb, dob, causal, scale, f"extreme sigma={sigma} scale={scale} V x{vmul}")
+
+
+def test_bwd_gradients_below_the_fp32_range():
+    # two causal tokens at scale 1 and sigma 4: query 1 weighs key 1 by about exp(-280), so the
+    # exact dQ and dK of that row are ~1.6e-124, below the smallest normal fp32 number; the GPU
+    # returns 0 there, within the representability floor (a randomised run found this case)
+    qb, kb, vb = make_qkv(1, 1, 2, 64, seed=2, sigma=4.0)
+    dob, _, _ = make_qkv(1, 1, 2, 64, seed=3)
+    ref = oracle.attention_bwd(qb, kb, vb, dob, True, 1.0)
+    assert 0 < np.abs(ref[1]).max() < FP32_MIN_NORMAL  # the case is what it claims to be
+    got, _ = check(qb, kb, vb, dob, True, 1.0, "gradients below the fp32 range")
+    assert all(np.isfinite(g).all() for g in got)
 
 
 def test_bwd_long_sequence():
