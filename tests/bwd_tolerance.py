@@ -9,8 +9,9 @@ rather than equal to it. TOL_FACTOR = 2 allows for that.
 The bounds are relative to the head's scale. In a head whose rows are all dominated by one key (a
 short head at a large scale), dS = P (dP - D) is everywhere a small difference of two large terms,
 dQ and dK are near zero, and the rounding of the forward's O, which enters D = dO . O, sets their
-error; relative bounds say nothing there. ``o_rounding_allowance`` bounds that error from the O the
-backward actually read; the GPU tests admit it where the relative bounds alone fail.
+error; relative bounds say nothing there. The same rounding is the whole error of D, which in a head
+of a few rows can be small in every row. ``o_rounding_allowance`` bounds those errors from the O the
+backward actually read; the GPU tests admit them where the relative bounds alone fail.
 """
 import json
 import os
@@ -25,17 +26,19 @@ RMS_TOL = TOL_FACTOR * MODEL["rms_max"]     # rms(gpu - ref) <= RMS_TOL * rms(re
 
 
 def o_rounding_allowance(qb, kb, vb, dob, causal, scale, o_used):
-    """Per element of dQ and dK, a bound on the error that the O the backward read (o_used, float64
-    [B, H, T, d], the forward's bf16 output) causes through D (float64 arrays shaped like dQ).
+    """Per element of dQ and dK, and per row of D, a bound on the error that the O the backward read
+    (o_used, float64 [B, H, T, d], the forward's bf16 output) causes through D: float64 arrays
+    shaped like dQ, dK and D.
 
     D_i moves by dD_i = dO_i . (O_used,i - O_i) plus its fp32 sum error (and dP_ij by its own), and
     dS_ij = P_ij (dP_ij - D_i) by P_ij times that, so dQ_i = scale sum_j dS_ij k_j moves by at most
-    scale |dD_i| sum_j P_ij |k_j| and dK_j = scale sum_i dS_ij q_i by scale sum_i P_ij |dD_i| |q_i|.
+    scale |dD_i| sum_j P_ij |k_j| and dK_j = scale sum_i dS_ij q_i by scale sum_i P_ij |dD_i| |q_i|;
+    D itself (an output too) by |dD_i|.
     """
     from exact_tiled_attention_07_amd.inputs import bf16_bits_to_f32
 
     B, H, T, d = qb.shape
-    aq, ak = np.empty((B, H, T, d)), np.empty((B, H, T, d))
+    aq, ak, ad = np.empty((B, H, T, d)), np.empty((B, H, T, d)), np.empty((B, H, T))
     hidden = ~np.tril(np.ones((T, T), dtype=bool)) if causal else np.zeros((T, T), dtype=bool)
     for b in range(B):
         for h in range(H):
@@ -50,4 +53,5 @@ def o_rounding_allowance(qb, kb, vb, dob, causal, scale, o_used):
             dD = np.abs((do * (o_used[b, h] - o)).sum(axis=1)) + fp32
             aq[b, h] = scale * dD[:, None] * (p @ np.abs(k))
             ak[b, h] = scale * (p.T @ (dD[:, None] * np.abs(q)))
-    return aq, ak
+            ad[b, h] = dD
+    return aq, ak, ad

@@ -63,7 +63,7 @@ def test_o_rounding_allowance_covers_a_head_dominated_by_one_key(causal):
     ref = oracle.attention_bwd(qb, kb, vb, dob, causal, 1.0)
     got = model.model_bwd(qb, kb, vb, dob, causal, 1.0)
     o16 = model.bf16(oracle.attention_fwd(qb, kb, vb, causal, 1.0)[0])
-    aq, ak = o_rounding_allowance(qb, kb, vb, dob, causal, 1.0, o16)
+    aq, ak, _ = o_rounding_allowance(qb, kb, vb, dob, causal, 1.0, o16)
     plain = [model.grad_stats(g, r) for g, r in zip(got[:2], ref[:2])]
     if not causal:  # (causal: row 0 sees one key, row 1 two; whichever way, the allowance must cover)
         assert any(s["max_ratio"] > ELEM_TOL or s["rms_ratio"] > RMS_TOL for s in plain)
@@ -80,6 +80,9 @@ def test_o_rounding_allowance_is_small_in_an_ordinary_head():
     qb, kb, vb, dob = model.inputs(1, 2, 300, 13)
     ref = oracle.attention_bwd(qb, kb, vb, dob, True, 0.125)
     o16 = model.bf16(oracle.attention_fwd(qb, kb, vb, True, 0.125)[0])
-    aq, ak = o_rounding_allowance(qb, kb, vb, dob, True, 0.125, o16)
+    aq, ak, ad = o_rounding_allowance(qb, kb, vb, dob, True, 0.125, o16)
     assert np.sqrt((aq ** 2).mean()) < 0.02 * np.sqrt((ref[0] ** 2).mean())
     assert np.sqrt((ak ** 2).mean()) < 0.02 * np.sqrt((ref[1] ** 2).mean())
+    # and D's allowance bounds the model's D error (the model's D is exactly dO . bf16(O))
+    got = model.model_bwd(qb, kb, vb, dob, True, 0.125)
+    assert np.all(np.abs(got[3] - ref[3]) <= 1.1 * ad + 1e-6 * np.abs(ref[3]))
