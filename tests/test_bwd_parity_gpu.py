@@ -18,6 +18,11 @@ of P sum to one, so dQ = scale dS K (dK = scale dS^T Q) is off by at most 2 scal
 (max|q|) times that. Every other element is held to the relative bounds alone. Every element
 also has the floor 2^-126, the smallest normal fp32 (and bf16) number: an exact gradient below it
 (a weight of exp(-300) times a small difference) cannot be represented by fp32 arithmetic at all.
+
+Where the relative bounds still fail (a short head whose rows are all dominated by one key, or whose
+D values are all small), the error that the forward's rounded O causes through D = dO . O is
+computed from the O the backward read and admitted with a 10% margin
+(bwd_tolerance.o_rounding_allowance); tests below keep the cases randomised runs found.
 """
 import math
 
