@@ -255,7 +255,9 @@ int fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o,
  *   o        [out] bf16 [B, H, T, d], device, 16-byte aligned
  *   lse      [out] fp32 [B, H, T], device, 4-byte aligned: natural-log logsumexp of the scaled scores
  *   scale, q_descale, k_descale, v_descale  finite and > 0: the scores are
- *            scale * (q_descale * q) . (k_descale * k), and V is v_descale * v
+ *            scale * (q_descale * q) . (k_descale * k), and V is v_descale * v; the factor the
+ *            kernel applies to the raw products, scale * q_descale * k_descale * log2(e), must lie
+ *            between 1e-37 and 3e38 (a normal fp32 number), else FA_ERR_INVALID_ARG
  *   B, H, T, d, causal, stream  as for fa_fwd (d = 64 or 128)
  * Numerics: fp32 accumulation and softmax; the probabilities are rounded to E4M3 (round to nearest
  * even, after scaling the largest weight of each row to 2^8) before the second product, which bounds

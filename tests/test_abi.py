@@ -385,6 +385,8 @@ def test_fp8_checks():
         assert call_fp8(vd=bad) == fa.FA_ERR_INVALID_ARG
         assert call_fp8(scale=bad) == fa.FA_ERR_INVALID_ARG
     assert call_fp8(qd=1e-30, kd=1e-30) == fa.FA_ERR_INVALID_ARG   # score factor underflows fp32
+    assert call_fp8(scale=1e38, qd=2.0, kd=2.0) == fa.FA_ERR_INVALID_ARG  # and overflows it
+    assert call_fp8(scale=1e30, qd=1.0, kd=1.0, T=0) == fa.FA_OK    # within range: accepted
     assert call_fp8(k=2 * A + 8) == fa.FA_ERR_ALIGNMENT
     assert call_fp8(lse=12 * A + 2) == fa.FA_ERR_ALIGNMENT
     assert call_fp8(o=A + 64) == fa.FA_ERR_INVALID_ARG             # output over q
