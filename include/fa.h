@@ -210,6 +210,8 @@ int fa_merge(const float* o_parts, const float* lse_parts, int n_parts, void* o,
  *   workspace  device memory of at least fa_splitkv_workspace_bytes(B, H, T, d, n_splits) bytes,
  *              16-byte aligned, owned by the caller: the fp32 partial results (O, then LSE);
  *              overwritten
+ *   workspace_bytes  its size; FA_ERR_INVALID_ARG if below that figure, or if the figure is 0 for a
+ *              non-empty problem (sizes or n_splits out of range)
  * Two kernels run in order on `stream`. No allocation. Returns FA_OK or a negative fa_status.
  */
 /* Workspace bytes fa_fwd_splitkv needs: n_splits * B*H*T * (d + 1) * 4 (fp32 O and LSE per range).
