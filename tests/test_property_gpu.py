@@ -3,8 +3,8 @@ derandomised so that every run draws the same cases).
 
 - fa_fwd: B, H, T <= 300, d in {64, 128}, causal or not, scale in {1/sqrt(d), 0.01, 1} and an
   input magnitude; every element within the bound derived from the kernel's roundings
-  (tests/fwd_bounds.py) and, except at sigma 2 with scale 1 (outside the regime it is written for),
-  at the dense tolerance;
+  (tests/fwd_bounds.py) and, for sigma <= 1 (the N(0,1) regime it is written for), at the dense
+  tolerance;
 - fa_bwd: the same ranges plus scale 0.3 and sigma 4, at the backward's tolerance (including its
   allowance for heads dominated by one key);
 - fa_fwd_sparse: random masks, one for every head or one per head, empty rows exact;
@@ -54,10 +54,11 @@ def test_random_shapes_against_oracle(B, H, T, d, causal, scale_kind, sigma, see
     o_ref, lse_ref = oracle.attention_fwd(qb, kb, vb, causal, scale)
     o, lse = o.float().cpu().numpy(), lse.cpu().numpy()
     label = f"B{B} H{H} T{T} d{d} causal={causal} scale={scale} sigma={sigma}"
-    if sigma <= 1.0 or scale <= 1.0 / math.sqrt(d):
-        # the stated tolerance is written for N(0,1) inputs (and holds on every row of the sigma-2
-        # workload at scale 1/sqrt(d)); at sigma 2 and scale 1 a weight's bf16 rounding times |v|
-        # up to 8 can exceed it where |O| < 2, and only the derived bound below applies
+    if sigma <= 1.0:
+        # the stated tolerance is written for N(0,1) inputs. At sigma 2 a non-top weight near 1,
+        # rounded to bf16 (2^-9 relative), times a |v| of up to ~8 can exceed it where |O| < 2 (rows
+        # with few keys at any scale, or sharp rows at scale 1), so only the derived bound below
+        # holds there (the every-row test of the sigma-2 workload C4 still asserts it)
         assert_parity(compare(o, lse, o_ref, lse_ref), label)
     # and every element within the bound derived from the kernel's roundings (tests/fwd_bounds.py)
     ro, rl = check_bounds(o, lse, o_ref, lse_ref, element_bounds(qb, kb, vb, causal, scale))
